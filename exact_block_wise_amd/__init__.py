@@ -1,0 +1,205 @@
+"""Exact block-wise softmax attention for MI355X (gfx950).
+
+A thin Python binding over the C-ABI library libexattn.so (declared in
+include/exattn.h).  It only marshals arguments: torch tensors provide device
+memory and the current HIP stream, and every step of the computation runs in
+the library's HIP kernels.  There is no fallback: if the library is missing
+or fails to load, every call raises.
+
+    o, lse = fwd(q, k, v)                        # [B,H,N,d] tensors
+    dq, dk, dv = bwd(q, k, v, o, do, lse)
+    o_parts, lse_parts = fwd_chunked(q, k, v, n_chunks=8)
+    o, lse = lse_merge(o_parts, lse_parts)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # imported first so the library binds to torch's HIP runtime
+
+__all__ = ["fwd", "fwd_chunked", "lse_merge", "bwd", "bwd_workspace_bytes",
+           "ExattnError", "library_path", "load", "ABI_VERSION",
+           "BWD_DQ_ACCUMULATE"]
+
+ABI_VERSION = 1
+BWD_DQ_ACCUMULATE = 1
+_F32, _BF16 = 0, 1
+_DTYPES = {torch.float32: _F32, torch.bfloat16: _BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+class ExattnError(RuntimeError):
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"{call} failed: {message} (status {status})")
+        self.status = status
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("sn", ctypes.c_int64)]
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nkv", ctypes.c_int32), ("d", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("EXATTN_LIB", os.path.join(_HERE, "libexattn.so"))
+
+
+def load() -> ctypes.CDLL:
+    """Load libexattn.so (once).  Raises if it is missing or mismatched."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ExattnError("load", -1, f"{path} not found; build it with "
+                          "`python -m exact_block_wise_amd.build`")
+    lib = ctypes.CDLL(path)
+    T, P = _Tensor, ctypes.POINTER(_Problem)
+    vp, fp, i32, u32, sz = (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                            ctypes.c_uint32, ctypes.c_size_t)
+    lib.attn_abi_version.restype = ctypes.c_int
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [P, T, T, T, T, fp, vp]
+    lib.attn_fwd_chunked.restype = ctypes.c_int
+    lib.attn_fwd_chunked.argtypes = [P, i32, T, T, T, fp, fp, vp]
+    lib.attn_lse_merge.restype = ctypes.c_int
+    lib.attn_lse_merge.argtypes = [i32, i32, i32, i32, i32, fp, fp, T, fp, vp]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd_workspace_bytes.argtypes = [P, u32]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [P, T, T, T, T, T, fp, T, T, T, vp, sz, u32, vp]
+    if lib.attn_abi_version() != ABI_VERSION:
+        raise ExattnError("load", -1, f"ABI version {lib.attn_abi_version()} != {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _check(call: str, st: int):
+    if st != 0:
+        raise ExattnError(call, st, load().attn_status_string(st).decode())
+
+
+def _desc(t: torch.Tensor) -> _Tensor:
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B,H,N,d] tensor, got shape {tuple(t.shape)}")
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return _Tensor(t.data_ptr(), _DTYPES[t.dtype], t.stride(0), t.stride(1), t.stride(2))
+
+
+def _problem(q, k, scale) -> _Problem:
+    B, H, Nq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return _Problem(B, H, Nq, k.shape[2], d, scale)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_f32_contig(t, shape, name):
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
+
+
+def fwd(q, k, v, scale=None, out=None, lse=None, out_dtype=None):
+    """Forward pass.  Returns (o [B,H,Nq,d], lse [B,H,Nq] float32)."""
+    lib = load()
+    B, H, Nq, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_f32_contig(lse, (B, H, Nq), "lse")
+    p = _problem(q, k, scale)
+    _check("attn_fwd", lib.attn_fwd(ctypes.byref(p), _desc(q), _desc(k), _desc(v), _desc(out),
+                                    lse.data_ptr(), _stream(q.device)))
+    return out, lse
+
+
+def fwd_chunked(q, k, v, n_chunks, scale=None, o_parts=None, lse_parts=None):
+    """Per-chunk partials over n_chunks key/value chunks, one launch.
+
+    Returns (o_parts [n,B,H,Nq,d] float32, lse_parts [n,B,H,Nq] float32).
+    """
+    lib = load()
+    B, H, Nq, d = q.shape
+    if o_parts is None:
+        o_parts = torch.empty((n_chunks, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_parts is None:
+        lse_parts = torch.empty((n_chunks, B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_f32_contig(o_parts, (n_chunks, B, H, Nq, d), "o_parts")
+    _check_f32_contig(lse_parts, (n_chunks, B, H, Nq), "lse_parts")
+    p = _problem(q, k, scale)
+    _check("attn_fwd_chunked",
+           lib.attn_fwd_chunked(ctypes.byref(p), n_chunks, _desc(q), _desc(k), _desc(v),
+                                o_parts.data_ptr(), lse_parts.data_ptr(), _stream(q.device)))
+    return o_parts, lse_parts
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse=None, out_dtype=torch.bfloat16):
+    """Exact merge of partials.  Returns (o [B,H,Nq,d], lse [B,H,Nq])."""
+    lib = load()
+    n, B, H, Nq, d = o_parts.shape
+    _check_f32_contig(o_parts, (n, B, H, Nq, d), "o_parts")
+    _check_f32_contig(lse_parts, (n, B, H, Nq), "lse_parts")
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_parts.device)
+    _check_f32_contig(lse, (B, H, Nq), "lse")
+    _check("attn_lse_merge",
+           lib.attn_lse_merge(n, B, H, Nq, d, o_parts.data_ptr(), lse_parts.data_ptr(),
+                              _desc(out), lse.data_ptr(), _stream(o_parts.device)))
+    return out, lse
+
+
+def bwd_workspace_bytes(q, k, accumulate_dq=False) -> int:
+    p = _problem(q, k, None)
+    return int(load().attn_bwd_workspace_bytes(ctypes.byref(p),
+                                               BWD_DQ_ACCUMULATE if accumulate_dq else 0))
+
+
+def bwd(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
+        accumulate_dq=False, workspace=None):
+    """Backward pass from the saved LSE.  Returns (dq, dk, dv).
+
+    With accumulate_dq the gradient is added to dq, which must be float32
+    (the chunked backward: pass the merged o and lse for every chunk).
+    """
+    lib = load()
+    if dq is None:
+        dq = (torch.zeros_like(q, dtype=torch.float32) if accumulate_dq else torch.empty_like(q))
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    B, H, Nq, d = q.shape
+    _check_f32_contig(lse, (B, H, Nq), "lse")
+    flags = BWD_DQ_ACCUMULATE if accumulate_dq else 0
+    p = _problem(q, k, scale)
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(p), flags)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("attn_bwd",
+           lib.attn_bwd(ctypes.byref(p), _desc(q), _desc(k), _desc(v), _desc(o), _desc(dout),
+                        lse.data_ptr(), _desc(dq), _desc(dk), _desc(dv), workspace.data_ptr(),
+                        workspace.numel(), flags, _stream(q.device)))
+    return dq, dk, dv

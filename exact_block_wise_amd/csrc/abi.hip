@@ -1,0 +1,206 @@
+// C-ABI entry points: host-side validation, then kernel dispatch on the
+// caller's stream.  Nothing here allocates, copies, synchronises or keeps
+// mutable state; an argument error returns before any work is enqueued.
+#include "../../include/exattn.h"
+
+#include <math.h>
+
+#include "kernels.hpp"
+
+using namespace exattn;
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool supported_d(int d) { return d == 64 || d == 80 || d == 128; }
+
+int elem_bytes(int dtype) { return dtype == ATTN_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16; }
+
+attn_status check_problem(const attn_problem* p) {
+  if (!p) return ATTN_E_INVALID;
+  if (p->B < 1 || p->H < 1 || p->Nq < 1 || p->Nkv < 1 || p->d < 1) return ATTN_E_INVALID;
+  if (!isfinite(p->scale)) return ATTN_E_INVALID;
+  if (!supported_d(p->d)) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// pointer, dtype, non-negative strides; then 16-byte vector access rules
+attn_status check_tensor(const attn_tensor& t) {
+  if (!t.ptr || !valid_dtype(t.dtype)) return ATTN_E_INVALID;
+  if (t.sb < 0 || t.sh < 0 || t.sn < 0) return ATTN_E_INVALID;
+  const int64_t vec = 16 / elem_bytes(t.dtype);
+  if (reinterpret_cast<uintptr_t>(t.ptr) % 16 != 0) return ATTN_E_UNSUPPORTED;
+  if (t.sb % vec || t.sh % vec || t.sn % vec) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status first_error(std::initializer_list<attn_status> sts) {
+  for (attn_status s : sts)
+    if (s != ATTN_OK) return s;
+  return ATTN_OK;
+}
+
+Strides strides_of(const attn_tensor& t) { return Strides{t.sb, t.sh, t.sn}; }
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+struct BwdLayout {
+  size_t dsum_bytes, dq_bytes, total;
+};
+
+BwdLayout bwd_layout(const attn_problem* p, int in_dtype, uint32_t flags) {
+  BwdLayout l{};
+  const size_t rows = (size_t)p->B * p->H * p->Nq;
+  l.dsum_bytes = round_up(rows * sizeof(float), kWsAlign);
+  const bool need_acc = in_dtype == ATTN_BF16 && !(flags & ATTN_BWD_DQ_ACCUMULATE);
+  l.dq_bytes = need_acc ? round_up(rows * p->d * sizeof(float), kWsAlign) : 0;
+  l.total = l.dsum_bytes + l.dq_bytes;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_string(attn_status st) {
+  switch (st) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_E_INVALID: return "ATTN_E_INVALID: invalid argument";
+    case ATTN_E_UNSUPPORTED: return "ATTN_E_UNSUPPORTED: head dim, stride or alignment not served";
+    case ATTN_E_WORKSPACE: return "ATTN_E_WORKSPACE: workspace missing or too small";
+    case ATTN_E_HIP: return "ATTN_E_HIP: HIP runtime error";
+  }
+  return "unknown attn_status";
+}
+
+attn_status attn_fwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                     attn_tensor o, float* lse, void* stream) {
+  attn_status st = first_error({check_problem(p), check_tensor(q), check_tensor(k),
+                                check_tensor(v), check_tensor(o)});
+  if (st != ATTN_OK) return st;
+  if (k.dtype != q.dtype || v.dtype != q.dtype) return ATTN_E_INVALID;
+  if (o.dtype != q.dtype && o.dtype != ATTN_F32) return ATTN_E_INVALID;
+  if (!lse) return ATTN_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
+  FwdArgs a{};
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.o = o.ptr; a.lse = lse;
+  a.qs = strides_of(q); a.ks = strides_of(k); a.vs = strides_of(v); a.os = strides_of(o);
+  a.B = p->B; a.H = p->H; a.Nq = p->Nq; a.Nkv = p->Nkv;
+  a.n_chunks = 1; a.chunk_len = p->Nkv;
+  a.scale = p->scale;
+  a.out_f32 = o.dtype == ATTN_F32;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(q.dtype == ATTN_BF16 ? launch_fwd_bf16(a, p->d, s) : launch_fwd_f32(a, p->d, s));
+}
+
+attn_status attn_fwd_chunked(const attn_problem* p, int32_t n_chunks, attn_tensor q,
+                             attn_tensor k, attn_tensor v, float* o_parts, float* lse_parts,
+                             void* stream) {
+  attn_status st = first_error({check_problem(p), check_tensor(q), check_tensor(k),
+                                check_tensor(v)});
+  if (st != ATTN_OK) return st;
+  if (n_chunks < 1) return ATTN_E_INVALID;
+  if (k.dtype != q.dtype || v.dtype != q.dtype) return ATTN_E_INVALID;
+  if (!o_parts || !lse_parts) return ATTN_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(o_parts) % 16 || reinterpret_cast<uintptr_t>(lse_parts) % 4)
+    return ATTN_E_UNSUPPORTED;
+  FwdArgs a{};
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.o = o_parts; a.lse = lse_parts;
+  a.qs = strides_of(q); a.ks = strides_of(k); a.vs = strides_of(v);
+  const int64_t d = p->d;
+  a.os = Strides{(int64_t)p->H * p->Nq * d, (int64_t)p->Nq * d, d};
+  a.o_chunk_stride = (int64_t)p->B * p->H * p->Nq * d;
+  a.lse_chunk_stride = (int64_t)p->B * p->H * p->Nq;
+  a.B = p->B; a.H = p->H; a.Nq = p->Nq; a.Nkv = p->Nkv;
+  a.n_chunks = n_chunks;
+  a.chunk_len = (int)(((int64_t)p->Nkv + n_chunks - 1) / n_chunks);
+  a.scale = p->scale;
+  a.out_f32 = 1;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(q.dtype == ATTN_BF16 ? launch_fwd_bf16(a, p->d, s) : launch_fwd_f32(a, p->d, s));
+}
+
+attn_status attn_lse_merge(int32_t n_parts, int32_t B, int32_t H, int32_t Nq, int32_t d,
+                           const float* o_parts, const float* lse_parts, attn_tensor o,
+                           float* lse, void* stream) {
+  if (n_parts < 1 || B < 1 || H < 1 || Nq < 1 || d < 1) return ATTN_E_INVALID;
+  if (!o_parts || !lse_parts || !lse) return ATTN_E_INVALID;
+  attn_status st = check_tensor(o);
+  if (st != ATTN_OK) return st;
+  if (d % 4) return ATTN_E_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(o_parts) % 16 || reinterpret_cast<uintptr_t>(lse_parts) % 4 ||
+      reinterpret_cast<uintptr_t>(lse) % 4)
+    return ATTN_E_UNSUPPORTED;
+  MergeArgs a{};
+  a.o_parts = o_parts; a.lse_parts = lse_parts; a.o = o.ptr; a.lse = lse;
+  a.os = strides_of(o);
+  a.n_parts = n_parts; a.B = B; a.H = H; a.Nq = Nq; a.d = d;
+  a.out_f32 = o.dtype == ATTN_F32;
+  return from_hip(launch_merge(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags) {
+  if (check_problem(p) != ATTN_OK) return 0;
+  // the accumulator is needed only for bf16 inputs without ACCUMULATE; report
+  // the larger layout since the dtype is not part of the query
+  return bwd_layout(p, ATTN_BF16, flags).total;
+}
+
+attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                     attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
+                     attn_tensor dk, attn_tensor dv, void* workspace, size_t workspace_bytes,
+                     uint32_t flags, void* stream) {
+  attn_status st = first_error({check_problem(p), check_tensor(q), check_tensor(k),
+                                check_tensor(v), check_tensor(o), check_tensor(dout),
+                                check_tensor(dq), check_tensor(dk), check_tensor(dv)});
+  if (st != ATTN_OK) return st;
+  if (flags & ~ATTN_BWD_DQ_ACCUMULATE) return ATTN_E_INVALID;
+  const int dt = q.dtype;
+  if (k.dtype != dt || v.dtype != dt || dout.dtype != dt) return ATTN_E_INVALID;
+  if (o.dtype != dt && o.dtype != ATTN_F32) return ATTN_E_INVALID;
+  if (dk.dtype != dt || dv.dtype != dt) return ATTN_E_INVALID;
+  const bool acc = flags & ATTN_BWD_DQ_ACCUMULATE;
+  if (acc ? dq.dtype != ATTN_F32 : dq.dtype != dt) return ATTN_E_INVALID;
+  if (!lse) return ATTN_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
+  const BwdLayout lay = bwd_layout(p, dt, flags);
+  if (!workspace || workspace_bytes < lay.total) return ATTN_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return ATTN_E_WORKSPACE;
+
+  BwdArgs a{};
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.o = o.ptr; a.dout = dout.ptr; a.lse = lse;
+  a.dq = dq.ptr; a.dk = dk.ptr; a.dv = dv.ptr;
+  a.qs = strides_of(q); a.ks = strides_of(k); a.vs = strides_of(v); a.os = strides_of(o);
+  a.dos = strides_of(dout); a.dqs = strides_of(dq); a.dks = strides_of(dk);
+  a.dvs = strides_of(dv);
+  a.dsum = static_cast<float*>(workspace);
+  a.B = p->B; a.H = p->H; a.Nq = p->Nq; a.Nkv = p->Nkv;
+  a.scale = p->scale;
+  a.o_f32 = o.dtype == ATTN_F32;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dt == ATTN_F32) {
+    a.dq_acc = nullptr;
+    a.zero_dq_acc = 0;
+    return from_hip(launch_bwd_f32(a, p->d, acc ? 1 : 0, s));
+  }
+  if (acc) {
+    a.dq_acc = static_cast<float*>(dq.ptr);
+    a.dqa = strides_of(dq);
+    a.zero_dq_acc = 0;
+    return from_hip(launch_bwd_bf16(a, p->d, 0, s));
+  }
+  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.dsum_bytes);
+  const int64_t d = p->d;
+  a.dqa = Strides{(int64_t)p->H * p->Nq * d, (int64_t)p->Nq * d, d};
+  a.zero_dq_acc = 1;
+  return from_hip(launch_bwd_bf16(a, p->d, 1, s));
+}
+
+}  // extern "C"

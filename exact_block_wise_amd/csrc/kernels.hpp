@@ -1,0 +1,65 @@
+// Kernel argument blocks and launcher declarations (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exattn {
+
+struct Strides {
+  int64_t sb, sh, sn;
+};
+
+// Forward over key rows [c*chunk_len, min((c+1)*chunk_len, Nkv)) for chunk
+// c in [0, n_chunks).  A plain forward is n_chunks = 1, chunk_len = Nkv.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  Strides qs, ks, vs, os;
+  int64_t o_chunk_stride;    // elements between chunks' outputs
+  int64_t lse_chunk_stride;  // elements between chunks' LSE rows
+  int B, H, Nq, Nkv;
+  int n_chunks, chunk_len;
+  float scale;
+  int out_f32;               // 1: o is fp32, 0: o is the input dtype
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;      // final dQ (input dtype), or the fp32 accumulator target
+  void* dk;
+  void* dv;
+  float* dsum;   // [B,H,Nq] workspace: D_i = dO_i . O_i
+  float* dq_acc; // fp32 accumulator, strides dqa
+  Strides qs, ks, vs, os, dos, dqs, dks, dvs, dqa;
+  int B, H, Nq, Nkv;
+  float scale;
+  int o_f32;       // o dtype is fp32
+  int zero_dq_acc; // preprocess clears dq_acc
+};
+
+struct MergeArgs {
+  const float* o_parts;
+  const float* lse_parts;
+  void* o;
+  float* lse;
+  Strides os;
+  int n_parts, B, H, Nq, d;
+  int out_f32;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int finalize_dq, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, int accumulate, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace exattn

@@ -1,0 +1,189 @@
+/*
+ * exattn.h -- C ABI of the exact block-wise attention library (libexattn.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Attention is a weighted average of value rows whose
+ * weights are the softmax of query-key dot products ("Training a Large Video
+ * Model on a Single Machine in a Day", section 3, "Flash Attention"
+ * paragraph).  With the scale inside the softmax, per (batch b, head h):
+ *
+ *     S   = scale * Q K^T                       (Nq x Nkv, never stored)
+ *     LSE = ln sum_j exp(S_ij)                  (per query row, natural log)
+ *     O   = exp(S - LSE) V                      (Nq x d)
+ *
+ * The library computes this block by block with an online softmax, so the
+ * Nq x Nkv weight matrix is never written to memory (same page, sections 1
+ * and 3: results of on-chip-sized blocks are combined into the final output;
+ * memory falls from O(N^2) to O(N)).  The result is exact up to floating
+ * point rounding, not an approximation.
+ *
+ * Conventions shared by every call:
+ *  - Tensors are [B, H, N, d] with the d (head dimension) stride equal to 1;
+ *    the B, H and N strides are free (in elements, see attn_tensor).  A
+ *    key/value chunk is therefore a strided view, never a copy.
+ *  - All data pointers are DEVICE pointers allocated and owned by the
+ *    caller.  The library never allocates, frees, copies to or from the host,
+ *    or synchronises.  Each call validates its arguments on the host,
+ *    enqueues its kernels on `stream` (a hipStream_t; NULL means the default
+ *    stream) and returns.  Results are ready when the stream reaches them.
+ *  - Validation happens before anything is enqueued: a call that returns an
+ *    error other than ATTN_E_HIP has enqueued no work and touched no memory.
+ *  - ATTN_E_HIP means a kernel launch was rejected by the HIP runtime; work
+ *    enqueued earlier in the same call may have run.
+ *  - No call keeps global mutable state, prints, throws or aborts.  Calls on
+ *    distinct streams may run concurrently from different host threads.
+ *  - Supported: d in {64, 80, 128}; inputs all F32 or all BF16.  bf16 inputs
+ *    use bf16 matrix-core products with fp32 accumulation; f32 inputs use
+ *    genuine fp32 products and accumulation.
+ */
+#ifndef EXATTN_H
+#define EXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = 1,      /* null pointer, non-positive size, mixed dtypes */
+  ATTN_E_UNSUPPORTED = 2,  /* valid but not served: d, stride, alignment   */
+  ATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than required   */
+  ATTN_E_HIP = 4           /* the HIP runtime rejected a launch            */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* A [B, H, N, d] tensor: element (b, h, n, c) lives at
+ * ptr + (b*sb + h*sh + n*sn + c) elements.  ptr must be 16-byte aligned and
+ * sn, sh, sb multiples of 8 (BF16) or 4 (F32) elements, so that a row of d
+ * values can be moved with 16-byte vector accesses. */
+typedef struct {
+  void* ptr;
+  int32_t dtype;           /* attn_dtype */
+  int64_t sb, sh, sn;
+} attn_tensor;
+
+/* Problem shape.  scale multiplies Q K^T inside the softmax (1/sqrt(d) for
+ * the usual attention). */
+typedef struct {
+  int32_t B, H, Nq, Nkv, d;
+  float scale;
+} attn_problem;
+
+/* attn_bwd flag: dq is F32 and the gradient is ADDED to it.  Used for the
+ * backward over key/value chunks, where dQ is the sum of the chunks'
+ * contributions. */
+#define ATTN_BWD_DQ_ACCUMULATE 1u
+
+/*
+ * attn_fwd -- forward pass: O and the per-row log-sum-exp.
+ *
+ *   q  [B,H,Nq,d], k and v [B,H,Nkv,d]: same dtype (F32 or BF16).
+ *   o  [B,H,Nq,d]: the input dtype, or F32 for any input (a partial that is
+ *      later merged by attn_lse_merge).  Written, never read.
+ *   lse [B,H,Nq] contiguous fp32: LSE_i = ln sum_j exp(scale q_i . k_j),
+ *      natural log, scale included.  Written, never read.
+ *
+ * The log-sum-exp is the one O(N) statistic the backward needs (weights are
+ * recomputed from it, not stored: the page's memory argument, section 4.1)
+ * and the one that lets partial results over disjoint key sets be merged
+ * exactly (attn_lse_merge).
+ */
+attn_status attn_fwd(const attn_problem* p, attn_tensor q, attn_tensor k,
+                     attn_tensor v, attn_tensor o, float* lse, void* stream);
+
+/*
+ * attn_fwd_chunked -- forward pass over n_chunks key/value chunks in one
+ * launch, producing the per-chunk partials that attn_lse_merge combines.
+ *
+ * Chunk c covers key rows [c*L, min((c+1)*L, Nkv)) with L = ceil(Nkv /
+ * n_chunks); a chunk with no rows yields O = 0 and LSE = -inf.  Exactly the
+ * same as n_chunks calls of attn_fwd on the chunk views with F32 outputs.
+ *
+ * This is the one-GPU share of the LV-XAttn setting (ICML 2025 poster
+ * "LV-XAttn", abstract): a small query block against large key/value blocks
+ * that stay where they are, each block producing a partial result.
+ *
+ *   q [B,H,Nq,d], k/v [B,H,Nkv,d] (F32 or BF16).
+ *   o_parts   [n_chunks,B,H,Nq,d] fp32 contiguous.  Written.
+ *   lse_parts [n_chunks,B,H,Nq]   fp32 contiguous.  Written.
+ */
+attn_status attn_fwd_chunked(const attn_problem* p, int32_t n_chunks,
+                             attn_tensor q, attn_tensor k, attn_tensor v,
+                             float* o_parts, float* lse_parts, void* stream);
+
+/*
+ * attn_lse_merge -- exact merge of partials over disjoint key/value sets.
+ *
+ * Because exp(LSE) of a union of key sets is the sum of the parts' exp(LSE):
+ *     M   = max_c LSE_c
+ *     LSE = M + ln sum_c exp(LSE_c - M)
+ *     O   = sum_c exp(LSE_c - LSE) O_c
+ * (the exact, output-preserving combination of the LV-XAttn abstract and
+ * lay summary).  A partial with LSE_c = -inf contributes nothing; a row whose
+ * partials are all -inf gets O = 0 and LSE = -inf.
+ *
+ *   o_parts   [n_parts,B,H,Nq,d] fp32 contiguous.  Read only.
+ *   lse_parts [n_parts,B,H,Nq]   fp32 contiguous.  Read only.
+ *   o   [B,H,Nq,d] F32 or BF16 (strided like any attn_tensor).  Written.
+ *   lse [B,H,Nq] fp32 contiguous.  Written.
+ * n_parts >= 1.  d must be a multiple of 4 (64, 80, 128 are).
+ */
+attn_status attn_lse_merge(int32_t n_parts, int32_t B, int32_t H, int32_t Nq,
+                           int32_t d, const float* o_parts,
+                           const float* lse_parts, attn_tensor o, float* lse,
+                           void* stream);
+
+/*
+ * attn_bwd_workspace_bytes -- device workspace attn_bwd needs for problem p
+ * and the given flags (0 if p is invalid).  The caller allocates it; its
+ * contents on entry do not matter.
+ */
+size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags);
+
+/*
+ * attn_bwd -- backward pass for the loss gradient dO, from the saved LSE.
+ *
+ * The weights are recomputed block by block from Q, K and the saved LSE,
+ * never loaded (the memory-for-compute trade of the AVION page, section 4.1,
+ * and the activation recomputation of the LV-XAttn abstract):
+ *     P  = exp(scale Q K^T - LSE)
+ *     dV = P^T dO,   dP = dO V^T,   D_i = dO_i . O_i,
+ *     dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
+ *
+ *   q, k, v, dout: the forward's inputs and the output gradient, one dtype.
+ *   o [B,H,Nq,d]: the forward output (F32 or BF16).  Only D = rowsum(dO*O)
+ *      is taken from it.
+ *   lse [B,H,Nq] fp32 contiguous: the forward's log-sum-exp.
+ *   o and lse must describe the FULL softmax row.  For a key/value chunk,
+ *   pass the merged O and LSE: each chunk then yields exactly its rows of dK
+ *   and dV, and its contribution to dQ (use ATTN_BWD_DQ_ACCUMULATE).
+ *   dq [B,H,Nq,d], dk/dv [B,H,Nkv,d]: the input dtype, written; except dq
+ *      under ATTN_BWD_DQ_ACCUMULATE, which must be F32 and is added to.
+ *   workspace: device memory of at least attn_bwd_workspace_bytes(p, flags)
+ *      bytes, 256-byte aligned; scratch for D and the fp32 dQ accumulator.
+ * dQ is accumulated with fp32 atomics, so results are not bitwise
+ * reproducible run to run; they are within rounding of the exact value.
+ */
+attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k,
+                     attn_tensor v, attn_tensor o, attn_tensor dout,
+                     const float* lse, attn_tensor dq, attn_tensor dk,
+                     attn_tensor dv, void* workspace, size_t workspace_bytes,
+                     uint32_t flags, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(attn_status st);
+
+/* ATTN_ABI_VERSION of the library that was loaded. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXATTN_H */

@@ -1,0 +1,136 @@
+"""The C-ABI library on the CPU: it loads, exports what include/exattn.h
+declares, and rejects invalid arguments on the host before any HIP call.
+
+No test here launches a kernel; the fake device pointers below are only
+inspected for null-ness and alignment by the library's validation code.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exattn.h")
+
+ebw = pytest.importorskip("exact_block_wise_amd")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ebw.library_path()):
+        pytest.fail("libexattn.so is not built (run __graft_entry__.build())")
+    return ebw.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "attn_abi_version", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd",
+        "attn_fwd_chunked", "attn_lse_merge", "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ebw.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings(lib):
+    assert lib.attn_abi_version() == ebw.ABI_VERSION
+    for st in range(5):
+        assert lib.attn_status_string(st).decode().startswith("ATTN_")
+    assert b"unknown" in lib.attn_status_string(99)
+
+
+FAKE = 0x10000000  # 16-byte aligned, never dereferenced on the host
+
+
+def T(ptr=FAKE, dtype=1, sb=12 * 1568 * 64, sh=1568 * 64, sn=64):
+    return ebw._Tensor(ptr, dtype, sb, sh, sn)
+
+
+def P(B=2, H=3, Nq=196, Nkv=196, d=64, scale=0.125):
+    return ebw._Problem(B, H, Nq, Nkv, d, scale)
+
+
+def fwd(lib, p=None, q=None, k=None, v=None, o=None, lse=FAKE):
+    return lib.attn_fwd(None if p is False else ctypes.byref(p or P()), q or T(), k or T(),
+                        v or T(), o or T(), lse, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, p=False) == INVALID
+    assert fwd(lib, p=P(B=0)) == INVALID
+    assert fwd(lib, p=P(Nkv=0)) == INVALID
+    assert fwd(lib, p=P(scale=float("nan"))) == INVALID
+    assert fwd(lib, p=P(d=96)) == UNSUPPORTED
+    assert fwd(lib, p=P(d=32)) == UNSUPPORTED
+    assert fwd(lib, q=T(ptr=0)) == INVALID
+    assert fwd(lib, lse=0) == INVALID
+    assert fwd(lib, k=T(dtype=0)) == INVALID            # mixed input dtypes
+    assert fwd(lib, q=T(dtype=7)) == INVALID
+    assert fwd(lib, q=T(dtype=0), k=T(dtype=0), v=T(dtype=0), o=T(dtype=1)) == INVALID
+    assert fwd(lib, q=T(ptr=FAKE + 8)) == UNSUPPORTED   # not 16-byte aligned
+    assert fwd(lib, v=T(sn=68)) == UNSUPPORTED          # bf16 row stride not a multiple of 8
+    assert fwd(lib, o=T(sh=-64)) == INVALID
+    assert fwd(lib, lse=FAKE + 2) == UNSUPPORTED
+
+
+def test_fwd_chunked_validation(lib):
+    def call(n=8, p=None, op=FAKE, lp=FAKE):
+        return lib.attn_fwd_chunked(ctypes.byref(p or P()), n, T(), T(), T(), op, lp, None)
+    assert call(n=0) == INVALID
+    assert call(op=0) == INVALID
+    assert call(op=FAKE + 4) == UNSUPPORTED
+    assert call(p=P(d=100)) == UNSUPPORTED
+
+
+def test_merge_validation(lib):
+    def call(n=8, B=4, H=32, Nq=128, d=128, op=FAKE, lp=FAKE, o=None, lse=FAKE):
+        return lib.attn_lse_merge(n, B, H, Nq, d, op, lp, o or T(), lse, None)
+    assert call(n=0) == INVALID
+    assert call(Nq=0) == INVALID
+    assert call(op=0) == INVALID
+    assert call(lse=0) == INVALID
+    assert call(d=66) == UNSUPPORTED
+    assert call(o=T(ptr=FAKE + 2)) == UNSUPPORTED
+
+
+def test_workspace_query(lib):
+    p = P(B=32, H=12, Nq=1568, Nkv=1568, d=64)
+    rows = 32 * 12 * 1568
+    rup = lambda x: (x + 255) // 256 * 256
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 0) == rup(rows * 4) + rup(rows * 64 * 4)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 1) == rup(rows * 4)
+    assert lib.attn_bwd_workspace_bytes(None, 0) == 0
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(P(d=96)), 0) == 0
+
+
+def bwd(lib, p=None, dq=None, flags=0, ws=FAKE, ws_bytes=1 << 40, o=None, dout=None, lse=FAKE):
+    return lib.attn_bwd(ctypes.byref(p or P()), T(), T(), T(), o or T(), dout or T(), lse,
+                        dq or T(), T(), T(), ws, ws_bytes, flags, None)
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, flags=2) == INVALID
+    assert bwd(lib, lse=0) == INVALID
+    assert bwd(lib, dout=T(dtype=0)) == INVALID
+    assert bwd(lib, dq=T(dtype=1), flags=1) == INVALID   # accumulate needs an fp32 dq
+    assert bwd(lib, dq=T(dtype=0), flags=0) == INVALID   # otherwise dq is the input dtype
+    assert bwd(lib, ws=0) == WORKSPACE
+    assert bwd(lib, ws_bytes=1024) == WORKSPACE
+    assert bwd(lib, ws=FAKE + 128) == WORKSPACE          # not 256-byte aligned
+    assert bwd(lib, p=P(d=48)) == UNSUPPORTED
+    assert bwd(lib, o=T(dtype=0), dq=T(dtype=0), flags=1, ws_bytes=0) == WORKSPACE

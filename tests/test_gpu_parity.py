@@ -1,0 +1,252 @@
+"""HIP kernels against the fp64 oracle, through the C-ABI (GPU only).
+
+Small cases are compared element by element on every output; the full-size
+workloads run in the benchmark's launch configuration and are compared on
+sampled heads (all outputs of those heads) plus invariants over every head.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_block_wise_amd import synth
+from gpu_util import (TOL_GRAD_FRO, check_fwd, check_grads, max_abs, rel_fro, to_dev,
+                      to_host)
+
+pytestmark = pytest.mark.gpu
+
+ebw = pytest.importorskip("exact_block_wise_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ebw.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_case(x, dtype, scale, check_bwd=True):
+    """fwd (+ bwd) on the GPU and in the oracle; returns the error summary."""
+    q, k, v, do = (to_dev(x[n], dtype) for n in ("q", "k", "v", "do"))
+    o, lse = ebw.fwd(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], scale)
+    errs = check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, dtype)
+    if check_bwd:
+        dq, dk, dv = ebw.bwd(q, k, v, o, do, lse, scale=scale)
+        torch.cuda.synchronize()
+        ref = oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale)
+        errs += tuple(check_grads([to_host(t) for t in (dq, dk, dv)], ref, dtype))
+    return errs
+
+
+SMALL = [
+    # (B, H, Nq, Nkv, d, dtype, q_mult)
+    (1, 2, 196, 196, 64, "bf16", 1.0),     # ragged tail in both directions
+    (1, 1, 64, 64, 64, "bf16", 1.0),       # exactly one key tile
+    (2, 2, 256, 384, 64, "bf16", 1.0),     # several query and key tiles
+    (1, 2, 300, 257, 80, "bf16", 1.0),     # d = 80, ragged
+    (1, 2, 130, 700, 128, "bf16", 1.0),    # d = 128, Nq != Nkv
+    (1, 1, 1, 1, 64, "bf16", 1.0),         # degenerate: one query, one key
+    (1, 2, 33, 1, 64, "bf16", 1.0),        # one key: O = v_1, dQ = dK = 0
+    (1, 1, 5, 3000, 64, "bf16", 1.0),      # tiny query block, long keys
+    (1, 2, 200, 200, 64, "bf16", 8.0),     # peaky softmax (running max stress)
+    (1, 2, 150, 170, 80, "bf16", 8.0),
+    (1, 2, 196, 196, 64, "f32", 1.0),
+    (1, 2, 100, 77, 80, "f32", 1.0),
+    (1, 1, 70, 130, 128, "f32", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:5])) + f"-{c[5]}-q{c[6]:g}")
+def test_small_parity(case):
+    B, H, Nq, Nkv, d, dtype, qm = case
+    _say(f"case {case}")
+    x = synth.random_case(zlib.crc32(repr(case).encode()), B, H, Nq, Nkv, d, dtype, q_mult=qm)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    run_case(x, dtype, scale)
+
+
+def test_tiny_f32_workload():
+    """The fp32 workload (1 x 2 heads, 196 tokens, d = 64) at full size."""
+    w = synth.WORKLOADS["tiny_f32"]
+    x = {n: synth.full_tensor(w.cid, n, w.B, w.H, w.Nq if n in ("q", "do") else w.Nkv, w.d,
+                              w.dtype) for n in ("q", "k", "v", "do")}
+    errs = run_case(x, "f32", w.scale)
+    _say(f"tiny_f32 errors {errs}")
+
+
+def test_strided_views():
+    """Q as a head-strided slice and K/V as views into wider buffers."""
+    g = np.random.Generator(np.random.PCG64(77))
+    B, H, Nq, Nkv, d = 2, 3, 150, 260, 64
+    big = synth.round_to_bf16(g.standard_normal((B, H + 2, Nq + 10, d), dtype=np.float32))
+    kv = synth.round_to_bf16(g.standard_normal((B, H, Nkv + 40, 2 * d), dtype=np.float32))
+    do = synth.round_to_bf16(g.standard_normal((B, H, Nq, d), dtype=np.float32))
+    qd, kvd = to_dev(big, "bf16"), to_dev(kv, "bf16")
+    q = qd[:, 1:H + 1, 5:Nq + 5, :]
+    k = kvd[:, :, 8:Nkv + 8, :d]
+    v = kvd[:, :, 8:Nkv + 8, d:]
+    x = {"q": big[:, 1:H + 1, 5:Nq + 5], "k": kv[:, :, 8:Nkv + 8, :d],
+         "v": kv[:, :, 8:Nkv + 8, d:], "do": do}
+    scale = 0.125
+    o, lse = ebw.fwd(q, k, v, scale=scale)
+    dq, dk, dv = ebw.bwd(q, k, v, o, to_dev(do, "bf16"), lse, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], scale)
+    check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16")
+    check_grads([to_host(t) for t in (dq, dk, dv)],
+                oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale), "bf16")
+
+
+def test_fp32_output_of_bf16_inputs():
+    x = synth.random_case(5, 1, 2, 100, 300, 128, "bf16")
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    o, lse = ebw.fwd(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], float(np.float32(128 ** -0.5)))
+    assert o.dtype == torch.float32
+    # fp32 output of bf16 products: no output rounding, so much tighter than 2e-2
+    assert max_abs(to_host(o), o_ref) < 4e-3
+    assert max_abs(to_host(lse), lse_ref) < 1e-3
+
+
+@pytest.mark.parametrize("n_chunks,Nkv,d", [(8, 1000, 128), (3, 500, 64), (8, 5, 64), (4, 4096, 80)])
+def test_chunked_forward_merge_backward(n_chunks, Nkv, d):
+    """KV chunk partials in one launch, exact LSE merge, chunk-by-chunk backward
+    with the merged O/LSE and dQ accumulation, against the unsplit oracle.
+    With Nkv < n_chunks some chunks are empty (LSE = -inf)."""
+    _say(f"chunked n={n_chunks} Nkv={Nkv} d={d}")
+    B, H, Nq = 2, 3, 70
+    x = synth.random_case(1000 + Nkv + d, B, H, Nq, Nkv, d, "bf16")
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o_parts, lse_parts = ebw.fwd_chunked(q, k, v, n_chunks, scale=scale)
+    o, lse = ebw.lse_merge(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    L = -(-Nkv // n_chunks)
+    bounds = [min(c * L, Nkv) for c in range(n_chunks)] + [Nkv]
+    # every partial against the oracle's partial
+    for b in range(B):
+        for h in range(H):
+            _, _, op_ref, lp_ref = oracle.head_chunked_fwd(x["q"][b, h], x["k"][b, h],
+                                                           x["v"][b, h], scale, bounds)
+            op, lp = to_host(o_parts[:, b, h]), to_host(lse_parts[:, b, h])
+            finite = np.isfinite(lp_ref)
+            assert np.array_equal(finite, np.isfinite(lp))
+            assert np.all(lp[~finite] == -np.inf) and np.all(op[~finite] == 0)
+            assert max_abs(lp[finite], lp_ref[finite]) < 1e-3
+            assert max_abs(op[finite], op_ref[finite]) < 4e-3
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], scale)
+    check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "merged")
+    # backward chunk by chunk, dK/dV written into views of the full tensors
+    dq = torch.zeros((B, H, Nq, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    for c in range(n_chunks):
+        lo, hi = bounds[c], bounds[c + 1]
+        if hi <= lo:
+            continue
+        ebw.bwd(q, k[:, :, lo:hi], v[:, :, lo:hi], o, do, lse, scale=scale, dq=dq,
+                dk=dk[:, :, lo:hi], dv=dv[:, :, lo:hi], accumulate_dq=True)
+    torch.cuda.synchronize()
+    ref = oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale)
+    check_grads([to_host(t) for t in (dq, dk, dv)], ref, "bf16", "chunked")
+
+
+def test_merge_kernel_against_oracle():
+    g = np.random.Generator(np.random.PCG64(31))
+    n, B, H, Nq, d = 5, 2, 3, 40, 80
+    op = g.standard_normal((n, B, H, Nq, d)).astype(np.float32)
+    lp = (g.standard_normal((n, B, H, Nq)) * 3).astype(np.float32)
+    lp[1] = -np.inf                      # an empty chunk everywhere
+    lp[:, 0, 0, 7] = -np.inf             # a row with no keys at all
+    o, lse = ebw.lse_merge(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(),
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.lse_merge(op, lp)
+    o_h, l_h = to_host(o), to_host(lse)
+    assert l_h[0, 0, 7] == -np.inf and np.all(o_h[0, 0, 7] == 0)
+    fin = np.isfinite(lse_ref)
+    assert max_abs(l_h[fin], lse_ref[fin]) < 1e-5
+    assert max_abs(o_h, o_ref) < 1e-5
+
+
+def test_fwd_is_deterministic_and_bwd_close_across_runs():
+    x = synth.random_case(3, 1, 2, 300, 300, 64, "bf16")
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o1, l1 = ebw.fwd(q, k, v)
+    o2, l2 = ebw.fwd(q, k, v)
+    g1 = ebw.bwd(q, k, v, o1, do, l1)
+    g2 = ebw.bwd(q, k, v, o1, do, l1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])   # dK, dV: no atomics
+    assert rel_fro(to_host(g1[0]), to_host(g2[0])) < 1e-2            # dQ: atomic order
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times
+# --------------------------------------------------------------------------
+
+def _upload_workload(w):
+    dev = {}
+    for n in ("q", "k", "v", "do"):
+        nn = w.Nq if n in ("q", "do") else w.Nkv
+        dev[n] = to_dev(synth.full_tensor(w.cid, n, w.B, w.H, nn, w.d, w.dtype), w.dtype)
+    return dev
+
+
+def _sample_heads(w, n=3):
+    g = np.random.Generator(np.random.PCG64(w.cid))
+    idx = g.choice(w.B * w.H, size=n, replace=False)
+    return [(int(i) // w.H, int(i) % w.H) for i in idx]
+
+
+@pytest.mark.parametrize("name", ["vit_b", "vit_l", "vit_h14", "xattn"])
+def test_full_size_workload(name):
+    w = synth.WORKLOADS[name]
+    _say(f"full-size {name}: upload")
+    dev = _upload_workload(w)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    if w.chunks > 1:
+        o_parts, lse_parts = ebw.fwd_chunked(q, k, v, w.chunks, scale=w.scale)
+        o, lse = ebw.lse_merge(o_parts, lse_parts)
+        del o_parts, lse_parts
+    else:
+        o, lse = ebw.fwd(q, k, v, scale=w.scale)
+    dq, dk, dv = ebw.bwd(q, k, v, o, do, lse, scale=w.scale)
+    torch.cuda.synchronize()
+    _say(f"full-size {name}: GPU done")
+    # invariants over every head: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i
+    dk_sum = dk.float().sum(dim=2)
+    dv_sum = dv.float().sum(dim=2)
+    do_sum = do.float().sum(dim=2)
+    dk_scale = dk.float().abs().sum(dim=2).clamp_min(1e-30)
+    assert float((dk_sum.abs() / dk_scale).max()) < 2e-2
+    assert float(((dv_sum - do_sum).abs() / dv.float().abs().sum(dim=2)).max()) < 2e-2
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    # sampled heads against the oracle, every output of the head
+    for b, h in _sample_heads(w):
+        hx = synth.workload_head(w, b, h)
+        if w.chunks > 1:
+            L = w.Nkv // w.chunks
+            bounds = list(range(0, w.Nkv + 1, L))
+            o_ref, lse_ref, _, _ = oracle.head_chunked_fwd(hx["q"], hx["k"], hx["v"], w.scale,
+                                                           bounds)
+        else:
+            o_ref, lse_ref = oracle.head_fwd(hx["q"], hx["k"], hx["v"], w.scale)
+        check_fwd(to_host(o[b, h]), to_host(lse[b, h]), o_ref, lse_ref, "bf16", f"{name}[{b},{h}]")
+        ref = oracle.head_bwd(hx["q"], hx["k"], hx["v"], hx["do"], w.scale)
+        errs = check_grads([to_host(t[b, h]) for t in (dq, dk, dv)], ref, "bf16",
+                           f"{name}[{b},{h}]")
+        _say(f"  head ({b},{h}) grad errors {['%.2e' % e for e in errs]}")
+    assert max(errs) < TOL_GRAD_FRO
