@@ -5,10 +5,10 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 that is already resident in HBM: the forward (for the long-KV cross-attention
 workload: the chunk partials in one launch plus the exact LSE merge) and the
-backward from the saved LSE.  Throughput is algorithmic flops (4 units
-forward + 10 units backward, one unit = B*H*Nq*Nkv*d multiply-adds... counted
-as flops below) over wall time measured with HIP events on the stream the
-library launches on.  Prints one JSON line.
+backward from the saved LSE.  Throughput is algorithmic flops over wall time
+measured with HIP events on the stream the library launches on: with one unit
+u = B*H*Nq*Nkv*d, the forward's two matrix products are 4u flops and the
+backward's five are 10u.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -104,53 +104,83 @@ def main():
     o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=tdt, device="cuda")
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(ebw.bwd_workspace_bytes(q, k), 1), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ebw.bwd_workspace_bytes(q, k) // 4, dtype=torch.float32, device="cuda")
     if w.chunks > 1:
         o_parts = torch.empty((w.chunks, w.B, w.H, w.Nq, w.d), dtype=torch.float32, device="cuda")
         lse_parts = torch.empty((w.chunks, w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
 
-    def forward():
-        if w.chunks > 1:
-            ebw.fwd_chunked(q, k, v, w.chunks, scale=w.scale, o_parts=o_parts, lse_parts=lse_parts)
-            ebw.lse_merge(o_parts, lse_parts, out=o, lse=lse)
-        else:
-            ebw.fwd(q, k, v, scale=w.scale, out=o, lse=lse)
-
-    def backward():
-        ebw.bwd(q, k, v, o, do, lse, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+    # The step, as single-kernel library calls (HIP events between the calls
+    # therefore time one kernel each).  Credited flops per call, in units of
+    # B*H*Nq*Nkv*d: forward 4; dK/dV 8 (S, dP, dV, dK); dQ 2 (dQ; its S and
+    # dP recomputation, 4 more, is extra work and not credited).
+    calls = []
+    if w.chunks > 1:
+        calls.append(("fwd_chunked", 4.0, 4.0, lambda: ebw.fwd_chunked(
+            q, k, v, w.chunks, scale=w.scale, o_parts=o_parts, lse_parts=lse_parts)))
+        calls.append(("lse_merge", 0.0, 0.0,
+                      lambda: ebw.lse_merge(o_parts, lse_parts, out=o, lse=lse)))
+    else:
+        calls.append(("fwd", 4.0, 4.0,
+                      lambda: ebw.fwd(q, k, v, scale=w.scale, out=o, lse=lse)))
+    calls.append(("bwd_preprocess", 0.0, 0.0, lambda: ebw.bwd_preprocess(o, do, ws)))
+    calls.append(("bwd_dkdv", 8.0, 8.0, lambda: ebw.bwd(
+        q, k, v, None, do, lse, scale=w.scale, dk=dk, dv=dv, workspace=ws,
+        d_precomputed=True, need_dq=False)))
+    calls.append(("bwd_dq", 2.0, 6.0, lambda: ebw.bwd(
+        q, k, v, None, do, lse, scale=w.scale, dq=dq, workspace=ws, d_precomputed=True,
+        need_dkdv=False)))
 
     for _ in range(args.warmup):
-        forward()
-        backward()
+        for c in calls:
+            c[3]()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    n = len(calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(K)]
     torch.cuda.synchronize()
-    t_start.record()
     for i in range(K):
         ev[i][0].record()
-        forward()
-        ev[i][1].record()
-        backward()
-        ev[i][2].record()
-    t_end.record()
+        for j, c in enumerate(calls):
+            c[3]()
+            ev[i][j + 1].record()
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    total_ms = ev[0][0].elapsed_time(ev[K - 1][n])
+    per_call = {c[0]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
+                for j, c in enumerate(calls)}
     ms = total_ms / K
 
     u = float(w.units)
     flops = 14.0 * u
     value = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    bwd_avg = float(np.mean(bwd_ms))
-    fwd_avg = float(np.mean(fwd_ms))
-    bwd_tflops = 10.0 * u / (bwd_avg * 1e-3) / 1e12
-    fwd_tflops = 4.0 * u / (fwd_avg * 1e-3) / 1e12
+    fwd_ms = sum(per_call[c[0]] for c in calls if c[0] in ("fwd", "fwd_chunked", "lse_merge"))
+    bwd_ms = ms - fwd_ms
+    kernels = {}
+    for name, credit, executed, _ in calls:
+        t = per_call[name]
+        kernels[name] = {"ms": round(t, 5)}
+        if credit:
+            kernels[name]["tflops"] = round(credit * u / (t * 1e-3) / 1e12, 3)
+            kernels[name]["executed_tflops"] = round(executed * u / (t * 1e-3) / 1e12, 3)
+    dom = max((c for c in calls if c[1] > 0), key=lambda c: per_call[c[0]])
+    dom_t = per_call[dom[0]]
+    if w.chunks > 1:
+        # long-KV cross-attention: HBM-bound; algorithmic bytes of the kernel
+        bpe = 2
+        kv_bytes = 2 * w.B * w.H * w.Nkv * w.d * bpe
+        q_bytes = w.B * w.H * w.Nq * w.d * bpe
+        alg = {"fwd_chunked": kv_bytes + q_bytes,
+               "bwd_dkdv": 2 * kv_bytes + 2 * q_bytes + 2 * w.B * w.H * w.Nq * 4,
+               "bwd_dq": 2 * q_bytes + q_bytes + 2 * w.B * w.H * w.Nq * 4}[dom[0]]
+        achieved = alg / (dom_t * 1e-3) / 1e9
+        roof = {"kernel": dom[0], "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None}
+    else:
+        achieved = dom[1] * u / (dom_t * 1e-3) / 1e12
+        roof = {"kernel": dom[0], "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
 
     line = {
         "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, video ViT-B N=1568",
@@ -168,15 +198,10 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
                    "kv_chunks": w.chunks, "scale": w.scale},
         "pct_of_peak": round(100.0 * value / peak, 2),
-        "fwd_ms": round(fwd_avg, 5),
-        "bwd_ms": round(bwd_avg, 5),
-        "fwd_tflops": round(fwd_tflops, 3),
-        "bwd_tflops": round(bwd_tflops, 3),
-        "roofline": {
-            "kernel": "attn_bwd (D preprocess + key/value-outer main + dQ cast)",
-            "bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(bwd_tflops / peak, 4), "traffic": None,
-        },
+        "fwd_ms": round(fwd_ms, 5),
+        "bwd_ms": round(bwd_ms, 5),
+        "kernels": kernels,
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -19,12 +19,15 @@ import os
 
 import torch  # imported first so the library binds to torch's HIP runtime
 
-__all__ = ["fwd", "fwd_chunked", "lse_merge", "bwd", "bwd_workspace_bytes",
-           "ExattnError", "library_path", "load", "ABI_VERSION",
-           "BWD_DQ_ACCUMULATE"]
+__all__ = ["fwd", "fwd_chunked", "lse_merge", "bwd", "bwd_preprocess",
+           "bwd_workspace_bytes", "ExattnError", "library_path", "load", "ABI_VERSION",
+           "BWD_DQ_ACCUMULATE", "BWD_D_PRECOMPUTED", "BWD_NO_DQ", "BWD_NO_DKDV"]
 
 ABI_VERSION = 1
 BWD_DQ_ACCUMULATE = 1
+BWD_D_PRECOMPUTED = 2
+BWD_NO_DQ = 4
+BWD_NO_DKDV = 8
 _F32, _BF16 = 0, 1
 _DTYPES = {torch.float32: _F32, torch.bfloat16: _BF16}
 
@@ -78,6 +81,8 @@ def load() -> ctypes.CDLL:
     lib.attn_lse_merge.argtypes = [i32, i32, i32, i32, i32, fp, fp, T, fp, vp]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [P, u32]
+    lib.attn_bwd_preprocess.restype = ctypes.c_int
+    lib.attn_bwd_preprocess.argtypes = [P, T, T, fp, vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [P, T, T, T, T, T, fp, T, T, T, vp, sz, u32, vp]
     if lib.attn_abi_version() != ABI_VERSION:
@@ -177,29 +182,59 @@ def bwd_workspace_bytes(q, k, accumulate_dq=False) -> int:
                                                BWD_DQ_ACCUMULATE if accumulate_dq else 0))
 
 
+def bwd_preprocess(o, dout, dsum=None):
+    """D = rowsum(dO * O) in fp32, [B,H,Nq] (the attn_bwd workspace layout)."""
+    lib = load()
+    B, H, Nq, d = o.shape
+    if dsum is None:
+        dsum = torch.empty((B, H, Nq), dtype=torch.float32, device=o.device)
+    if dsum.dtype != torch.float32 or not dsum.is_contiguous() or dsum.numel() < B * H * Nq:
+        raise ValueError("dsum must be contiguous float32 with at least B*H*Nq elements")
+    p = _Problem(B, H, Nq, Nq, d, 1.0)
+    _check("attn_bwd_preprocess", lib.attn_bwd_preprocess(ctypes.byref(p), _desc(o), _desc(dout),
+                                                          dsum.data_ptr(), _stream(o.device)))
+    return dsum
+
+
+def _desc_or_null(t):
+    return _desc(t) if t is not None else _Tensor(None, _BF16, 0, 0, 0)
+
+
 def bwd(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
-        accumulate_dq=False, workspace=None):
+        accumulate_dq=False, workspace=None, d_precomputed=False, need_dq=True,
+        need_dkdv=True):
     """Backward pass from the saved LSE.  Returns (dq, dk, dv).
 
-    With accumulate_dq the gradient is added to dq, which must be float32
-    (the chunked backward: pass the merged o and lse for every chunk).
+    accumulate_dq: the gradient is added to dq, which must be float32 (the
+      chunked backward: pass the merged o and lse for every chunk).
+    d_precomputed: `workspace` already holds D = rowsum(dO * O) (see
+      bwd_preprocess); o may then be None.
+    need_dq / need_dkdv: compute only one half (the other outputs are None).
     """
     lib = load()
-    if dq is None:
+    if need_dq and dq is None:
         dq = (torch.zeros_like(q, dtype=torch.float32) if accumulate_dq else torch.empty_like(q))
-    if dk is None:
+    if need_dkdv and dk is None:
         dk = torch.empty_like(k)
-    if dv is None:
+    if need_dkdv and dv is None:
         dv = torch.empty_like(v)
     B, H, Nq, d = q.shape
     _check_f32_contig(lse, (B, H, Nq), "lse")
-    flags = BWD_DQ_ACCUMULATE if accumulate_dq else 0
+    flags = ((BWD_DQ_ACCUMULATE if accumulate_dq else 0) |
+             (BWD_D_PRECOMPUTED if d_precomputed else 0) |
+             (0 if need_dq else BWD_NO_DQ) | (0 if need_dkdv else BWD_NO_DKDV))
     p = _problem(q, k, scale)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(p), flags)
     if workspace is None:
+        if d_precomputed:
+            raise ValueError("d_precomputed needs the workspace that holds D")
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check("attn_bwd",
-           lib.attn_bwd(ctypes.byref(p), _desc(q), _desc(k), _desc(v), _desc(o), _desc(dout),
-                        lse.data_ptr(), _desc(dq), _desc(dk), _desc(dv), workspace.data_ptr(),
-                        workspace.numel(), flags, _stream(q.device)))
-    return dq, dk, dv
+           lib.attn_bwd(ctypes.byref(p), _desc(q), _desc(k), _desc(v), _desc_or_null(o),
+                        _desc(dout), lse.data_ptr(),
+                        _desc_or_null(dq if need_dq else None),
+                        _desc_or_null(dk if need_dkdv else None),
+                        _desc_or_null(dv if need_dkdv else None),
+                        workspace.data_ptr(), ws_bytes, flags, _stream(q.device)))
+    return (dq if need_dq else None, dk if need_dkdv else None, dv if need_dkdv else None)

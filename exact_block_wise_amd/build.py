@@ -46,15 +46,20 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, out_dir: str | None = None) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def build(verbose: bool = False, out_dir: str | None = None,
+          extra_flags: list[str] | None = None) -> str:
+    """Compile every source and link the shared library; returns its path.
+
+    extra_flags are appended to every compile (e.g. -D tile choices).
+    """
     cc = hipcc()
     obj_dir = os.path.join(out_dir or HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     jobs = []
     for src in SOURCES:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        jobs.append((obj, [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, [cc, *HIPCC_FLAGS, *(extra_flags or []), "-c",
+                           os.path.join(CSRC, src), "-o", obj]))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         for out in ex.map(lambda j: _run(j[1]), jobs):
             if verbose and out:

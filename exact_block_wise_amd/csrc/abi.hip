@@ -49,18 +49,15 @@ Strides strides_of(const attn_tensor& t) { return Strides{t.sb, t.sh, t.sn}; }
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 
-struct BwdLayout {
-  size_t dsum_bytes, dq_bytes, total;
-};
+size_t dsum_bytes(const attn_problem* p) {
+  return round_up((size_t)p->B * p->H * p->Nq * sizeof(float), kWsAlign);
+}
 
-BwdLayout bwd_layout(const attn_problem* p, int in_dtype, uint32_t flags) {
-  BwdLayout l{};
-  const size_t rows = (size_t)p->B * p->H * p->Nq;
-  l.dsum_bytes = round_up(rows * sizeof(float), kWsAlign);
-  const bool need_acc = in_dtype == ATTN_BF16 && !(flags & ATTN_BWD_DQ_ACCUMULATE);
-  l.dq_bytes = need_acc ? round_up(rows * p->d * sizeof(float), kWsAlign) : 0;
-  l.total = l.dsum_bytes + l.dq_bytes;
-  return l;
+// o / dout dtypes the preprocess serves: dout BF16 with o BF16 or F32;
+// dout F32 with o F32
+bool pre_dtypes_ok(int o_dtype, int do_dtype) {
+  return do_dtype == ATTN_BF16 ? (o_dtype == ATTN_BF16 || o_dtype == ATTN_F32)
+                               : o_dtype == ATTN_F32;
 }
 
 }  // namespace
@@ -147,31 +144,54 @@ attn_status attn_lse_merge(int32_t n_parts, int32_t B, int32_t H, int32_t Nq, in
 }
 
 size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags) {
+  (void)flags;
   if (check_problem(p) != ATTN_OK) return 0;
-  // the accumulator is needed only for bf16 inputs without ACCUMULATE; report
-  // the larger layout since the dtype is not part of the query
-  return bwd_layout(p, ATTN_BF16, flags).total;
+  return dsum_bytes(p);
+}
+
+attn_status attn_bwd_preprocess(const attn_problem* p, attn_tensor o, attn_tensor dout,
+                                float* dsum, void* stream) {
+  attn_status st = first_error({check_problem(p), check_tensor(o), check_tensor(dout)});
+  if (st != ATTN_OK) return st;
+  if (!pre_dtypes_ok(o.dtype, dout.dtype)) return ATTN_E_INVALID;
+  if (!dsum) return ATTN_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(dsum) % 4) return ATTN_E_UNSUPPORTED;
+  BwdArgs a{};
+  a.o = o.ptr; a.dout = dout.ptr; a.dsum = dsum;
+  a.os = strides_of(o); a.dos = strides_of(dout);
+  a.B = p->B; a.H = p->H; a.Nq = p->Nq; a.Nkv = p->Nkv;
+  a.o_f32 = o.dtype == ATTN_F32;
+  return from_hip(launch_bwd_pre(a, p->d, dout.dtype == ATTN_BF16,
+                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
 attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_tensor v,
                      attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
                      attn_tensor dk, attn_tensor dv, void* workspace, size_t workspace_bytes,
                      uint32_t flags, void* stream) {
+  constexpr uint32_t kAll = ATTN_BWD_DQ_ACCUMULATE | ATTN_BWD_D_PRECOMPUTED | ATTN_BWD_NO_DQ |
+                            ATTN_BWD_NO_DKDV;
+  if (flags & ~kAll) return ATTN_E_INVALID;
+  const bool acc = flags & ATTN_BWD_DQ_ACCUMULATE;
+  const bool pre_done = flags & ATTN_BWD_D_PRECOMPUTED;
+  const bool do_dq = !(flags & ATTN_BWD_NO_DQ);
+  const bool do_dkdv = !(flags & ATTN_BWD_NO_DKDV);
+  if (!do_dq && !do_dkdv) return ATTN_E_INVALID;
   attn_status st = first_error({check_problem(p), check_tensor(q), check_tensor(k),
-                                check_tensor(v), check_tensor(o), check_tensor(dout),
-                                check_tensor(dq), check_tensor(dk), check_tensor(dv)});
+                                check_tensor(v), check_tensor(dout),
+                                pre_done ? ATTN_OK : check_tensor(o),
+                                do_dq ? check_tensor(dq) : ATTN_OK,
+                                do_dkdv ? check_tensor(dk) : ATTN_OK,
+                                do_dkdv ? check_tensor(dv) : ATTN_OK});
   if (st != ATTN_OK) return st;
-  if (flags & ~ATTN_BWD_DQ_ACCUMULATE) return ATTN_E_INVALID;
   const int dt = q.dtype;
   if (k.dtype != dt || v.dtype != dt || dout.dtype != dt) return ATTN_E_INVALID;
-  if (o.dtype != dt && o.dtype != ATTN_F32) return ATTN_E_INVALID;
-  if (dk.dtype != dt || dv.dtype != dt) return ATTN_E_INVALID;
-  const bool acc = flags & ATTN_BWD_DQ_ACCUMULATE;
-  if (acc ? dq.dtype != ATTN_F32 : dq.dtype != dt) return ATTN_E_INVALID;
+  if (!pre_done && !pre_dtypes_ok(o.dtype, dt)) return ATTN_E_INVALID;
+  if (do_dkdv && (dk.dtype != dt || dv.dtype != dt)) return ATTN_E_INVALID;
+  if (do_dq && (acc ? dq.dtype != ATTN_F32 : dq.dtype != dt)) return ATTN_E_INVALID;
   if (!lse) return ATTN_E_INVALID;
   if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
-  const BwdLayout lay = bwd_layout(p, dt, flags);
-  if (!workspace || workspace_bytes < lay.total) return ATTN_E_WORKSPACE;
+  if (!workspace || workspace_bytes < dsum_bytes(p)) return ATTN_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return ATTN_E_WORKSPACE;
 
   BwdArgs a{};
@@ -185,22 +205,12 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_t
   a.scale = p->scale;
   a.o_f32 = o.dtype == ATTN_F32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dt == ATTN_F32) {
-    a.dq_acc = nullptr;
-    a.zero_dq_acc = 0;
-    return from_hip(launch_bwd_f32(a, p->d, acc ? 1 : 0, s));
+  if (!pre_done) {
+    const hipError_t e = launch_bwd_pre(a, p->d, dt == ATTN_BF16, s);
+    if (e != hipSuccess) return ATTN_E_HIP;
   }
-  if (acc) {
-    a.dq_acc = static_cast<float*>(dq.ptr);
-    a.dqa = strides_of(dq);
-    a.zero_dq_acc = 0;
-    return from_hip(launch_bwd_bf16(a, p->d, 0, s));
-  }
-  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.dsum_bytes);
-  const int64_t d = p->d;
-  a.dqa = Strides{(int64_t)p->H * p->Nq * d, (int64_t)p->Nq * d, d};
-  a.zero_dq_acc = 1;
-  return from_hip(launch_bwd_bf16(a, p->d, 1, s));
+  if (dt == ATTN_F32) return from_hip(launch_bwd_f32(a, p->d, do_dkdv, do_dq, acc, s));
+  return from_hip(launch_bwd_bf16(a, p->d, do_dkdv, do_dq, acc, s));
 }
 
 }  // extern "C"

@@ -11,11 +11,12 @@
 
 #include <math.h>
 
+
 namespace exattn {
 
 // --------------------------------------------------------------------------
-// Preprocess: D_i = sum_c dO_ic O_ic in fp32, one 16-lane group per row;
-// optionally clears the row of the fp32 dQ accumulator.
+// Preprocess: D_i = sum_c dO_ic O_ic in fp32, one 16-lane group per row.
+// (D_i also equals sum_j P_ij dP_ij, the row term of the softmax Jacobian.)
 // --------------------------------------------------------------------------
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int d) {
@@ -33,66 +34,53 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int d) {
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
   if (li == 0) a.dsum[row] = acc;
-  if (a.zero_dq_acc) {
-    float* dqr = a.dq_acc + b * a.dqa.sb + h * a.dqa.sh + (int64_t)i * a.dqa.sn;
-    for (int c = li; c < d; c += 16) dqr[c] = 0.f;
-  }
 }
 
 // --------------------------------------------------------------------------
-// bf16 main kernel, key/value-outer.
+// bf16 dK / dV kernel, key/value-outer.
 //
-// Workgroup: 4 waves own 128 key rows (32 each); K and V of those rows stay
-// in registers as matrix-core operands for the whole query loop, and the
-// fp32 dK, dV accumulators stay in registers too.  The query loop walks
-// 64-row tiles of Q, dO (staged in LDS both row-major and transposed), LSE
-// and D.  Per tile and wave:
+// Workgroup: 4 waves, each owning KW key rows (KW = 32 or 64).  K and V of a
+// wave's rows stay in registers as matrix-core operands for the whole query
+// loop, and so do the fp32 dK, dV accumulators.  The query loop walks 64-row
+// tiles of Q and dO, staged row-major in LDS and double-buffered (the next
+// tile's global loads are in flight while the current one is used).  Per
+// tile and 32-row query block:
 //   S = Q K^T, dP = dO V^T       (lane owns one key column, 16 query rows)
-//   P, dS elementwise            (fp32)
-//   dV += P^T dO, dK += dS^T Q   (accumulator entries reused as operands)
-// then dS goes to LDS and the 4 waves compute this tile's dQ = dS K over all
-// 128 keys, added to the fp32 accumulator with atomics.
+//   P = exp(S - LSE), dS = P (dP - D)           (fp32, registers)
+//   dV += P^T dO, dK += dS^T Q   (accumulators reused as A operands; dO and
+//                                 Q columns read with LDS transpose reads)
+// Query rows past Nq arrive as zeros with LSE = +inf (P = 0); key rows past
+// Nkv are zero and their gradients are never stored.
 // --------------------------------------------------------------------------
 namespace bwdk {
-constexpr int BN = 128;
 constexpr int BM = 64;
 constexpr int NT = 256;
 }  // namespace bwdk
 
 template <int D>
-struct BwdLds {
+struct DkdvLds {
   static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int RS = D + 8;               // row-major tiles
-  static constexpr int TS = bwdk::BM + 4;        // transposed Q / dO tiles
-  static constexpr int KTS = bwdk::BN + 8;       // transposed K
-  static constexpr int SS = bwdk::BN + 8;        // dS [q][key]
-  static constexpr int q_off = 0;
-  static constexpr int do_off = q_off + bwdk::BM * RS;
-  static constexpr int qt_off = do_off + bwdk::BM * RS;
-  static constexpr int dot_off = qt_off + DP * TS;
-  static constexpr int kt_off = dot_off + DP * TS;
-  static constexpr int ds_off = kt_off + DP * KTS;
-  static constexpr int n_bf16 = ds_off + bwdk::BM * SS;
-  static constexpr int bytes = n_bf16 * 2 + 2 * bwdk::BM * 4;
+  static constexpr int RS = DP + 8;                          // row stride of Q, dO tiles
+  static constexpr int tile = bwdk::BM * RS;
+  static constexpr int n_bf16 = 4 * tile;                    // Q, dO x double buffer
+  static constexpr int bytes = n_bf16 * 2 + 2 * 2 * bwdk::BM * 4;  // + (LSE, D) x 2
 };
 
-template <int D>
-__global__ __launch_bounds__(bwdk::NT) void bwd_bf16_kernel(BwdArgs a) {
+template <int D, int KW>
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   using namespace bwdk;
-  using L = BwdLds<D>;
-  constexpr int DP = L::DP;
-  constexpr int NDB = DP / 32;
-  constexpr int KC = D / 16;
+  using L = DkdvLds<D>;
+  constexpr int DP = L::DP, NDB = DP / 32, KC = D / 16, RS = L::RS;
+  constexpr int NCB = KW / 32;                 // 32-row key blocks per wave
+  // pin dK/dV in AGPRs only in the one-wave-per-SIMD instances, where the
+  // registers fit without spilling (see mfma32_agpr)
+  constexpr bool kPinAcc = KW == 64 || D > 80;
+  constexpr int BN = 4 * KW;                   // key rows per workgroup
+  constexpr int CH = BM * (D / 8);             // 16-byte pieces per Q (or dO) tile
+  constexpr int PT = (CH + NT - 1) / NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16* const lds = reinterpret_cast<bf16*>(smem);
-  bf16* const Qs = lds + L::q_off;
-  bf16* const dOs = lds + L::do_off;
-  bf16* const Qt = lds + L::qt_off;
-  bf16* const dOt = lds + L::dot_off;
-  bf16* const Kt = lds + L::kt_off;
-  bf16* const dSs = lds + L::ds_off;
-  float* const lse2s = reinterpret_cast<float*>(lds + L::n_bf16);
-  float* const Ds = lse2s + BM;
+  float* const stats = reinterpret_cast<float*>(lds + L::n_bf16);  // [2][LSE2 | D][BM]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ln = lane & 31, g = lane >> 5;
@@ -110,91 +98,100 @@ __global__ __launch_bounds__(bwdk::NT) void bwd_bf16_kernel(BwdArgs a) {
   const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh;
   const float* lsep = a.lse + ((int64_t)b * a.H + h) * a.Nq;
   const float* dsp = a.dsum + ((int64_t)b * a.H + h) * a.Nq;
-  float* dqp = a.dq_acc + b * a.dqa.sb + h * a.dqa.sh;
 
-  const int k0 = kb * BN;             // first key row of the workgroup
-  const int kw = k0 + 32 * w;         // first key row of this wave
+  const int kw = kb * BN + KW * w;             // first key row of this wave
   const bool wave_active = kw < a.Nkv;
-  const int krow = kw + ln;
-  const bool kvalid = krow < a.Nkv;
   const bf16x8 zero8 = {};
 
-  // this wave's K and V rows as B operands (lane: key krow, d 16kc+8g..+7)
-  bf16x8 kreg[KC], vreg[KC];
+  // this wave's K and V rows as B operands (lane: key kw + 32cb + ln,
+  // d = 16kc + 8g .. +7)
+  bf16x8 kreg[NCB][KC], vreg[NCB][KC];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    kreg[kc] = kvalid ? load_bf16x8(kp + (int64_t)krow * a.ks.sn + 16 * kc + 8 * g) : zero8;
-    vreg[kc] = kvalid ? load_bf16x8(vp + (int64_t)krow * a.vs.sn + 16 * kc + 8 * g) : zero8;
-  }
-  // K^T of the workgroup's 128 keys for the dQ product; padding rows zero
-  for (int e = tid; e < BN * (D / 8); e += NT) {
-    const int r = e % BN, cc = e / BN;
-    bf16x8 val = zero8;
-    if (k0 + r < a.Nkv) val = load_bf16x8(kp + (int64_t)(k0 + r) * a.ks.sn + 8 * cc);
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int krow = kw + 32 * cb + ln;
+    const bool ok = krow < a.Nkv;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Kt[(8 * cc + i) * L::KTS + r] = val[i];
-  }
-  if constexpr (DP != D) {
-    for (int i = tid; i < (DP - D) * L::KTS; i += NT) Kt[D * L::KTS + i] = (bf16)0.f;
-    for (int i = tid; i < (DP - D) * L::TS; i += NT) {
-      Qt[D * L::TS + i] = (bf16)0.f;
-      dOt[D * L::TS + i] = (bf16)0.f;
+    for (int kc = 0; kc < KC; ++kc) {
+      kreg[cb][kc] = ok ? load_bf16x8(kp + (int64_t)krow * a.ks.sn + 16 * kc + 8 * g) : zero8;
+      vreg[cb][kc] = ok ? load_bf16x8(vp + (int64_t)krow * a.vs.sn + 16 * kc + 8 * g) : zero8;
     }
   }
 
-  f32x16 dk[NDB], dv[NDB];
+  bf16x8 pq[PT], pd[PT];
+  float pst = 0.f;
+  auto load_tile = [&](int q0) {
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
-  }
-  const float sl2 = a.scale * kLog2e;
-
-  for (int q0 = 0; q0 < a.Nq; q0 += BM) {
-    __syncthreads();
-    // Q and dO tiles: row-major (consecutive threads along a row) ...
-    for (int e = tid; e < BM * (D / 8); e += NT) {
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
       const int r = e / (D / 8), cc = e % (D / 8);
-      bf16x8 qv = zero8, dv8 = zero8;
-      if (q0 + r < a.Nq) {
-        qv = load_bf16x8(qp + (int64_t)(q0 + r) * a.qs.sn + 8 * cc);
-        dv8 = load_bf16x8(dop + (int64_t)(q0 + r) * a.dos.sn + 8 * cc);
-      }
-      *reinterpret_cast<bf16x8*>(&Qs[r * L::RS + 8 * cc]) = qv;
-      *reinterpret_cast<bf16x8*>(&dOs[r * L::RS + 8 * cc]) = dv8;
+      const bool ok = e < CH && q0 + r < a.Nq;
+      pq[u] = ok ? load_bf16x8(qp + (int64_t)(q0 + r) * a.qs.sn + 8 * cc) : zero8;
+      pd[u] = ok ? load_bf16x8(dop + (int64_t)(q0 + r) * a.dos.sn + 8 * cc) : zero8;
     }
-    // ... and transposed (consecutive threads along a column)
-    for (int e = tid; e < BM * (D / 8); e += NT) {
-      const int r = e % BM, cc = e / BM;
-      bf16x8 qv = zero8, dv8 = zero8;
-      if (q0 + r < a.Nq) {
-        qv = load_bf16x8(qp + (int64_t)(q0 + r) * a.qs.sn + 8 * cc);
-        dv8 = load_bf16x8(dop + (int64_t)(q0 + r) * a.dos.sn + 8 * cc);
-      }
+    if (tid < 2 * BM) {
+      const int r = tid & (BM - 1);
+      const bool ok = q0 + r < a.Nq;
+      pst = tid < BM ? (ok ? lsep[q0 + r] * kLog2e : INFINITY) : (ok ? dsp[q0 + r] : 0.f);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    bf16* Qs = lds + buf * 2 * L::tile;
+    bf16* dOs = Qs + L::tile;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        Qt[(8 * cc + i) * L::TS + r] = qv[i];
-        dOt[(8 * cc + i) * L::TS + r] = dv8[i];
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      if (e < CH) {
+        const int r = e / (D / 8), cc = e % (D / 8);
+        *reinterpret_cast<bf16x8*>(&Qs[r * RS + 8 * cc]) = pq[u];
+        *reinterpret_cast<bf16x8*>(&dOs[r * RS + 8 * cc]) = pd[u];
       }
     }
-    if (tid < BM) {
-      const bool ok = q0 + tid < a.Nq;
-      // rows past Nq get P = exp2(-inf) = 0
-      lse2s[tid] = ok ? lsep[q0 + tid] * kLog2e : INFINITY;
-      Ds[tid] = ok ? dsp[q0 + tid] : 0.f;
-    }
-    __syncthreads();
+    if (tid < 2 * BM) stats[buf * 2 * BM + tid] = pst;
+  };
 
-    if (wave_active) {
+  f32x16 dk[NCB][NDB], dv[NCB][NDB];
 #pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      dk[cb][i] = f32x16{};
+      dv[cb][i] = f32x16{};
+    }
+  const float sl2 = a.scale * kLog2e;
+  const int nqt = (a.Nq + BM - 1) / BM;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int it = 0; it < nqt; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nqt) load_tile((it + 1) * BM);
+    if (wave_active) {
+      const bf16* Qs = lds + buf * 2 * L::tile;
+      const bf16* dOs = Qs + L::tile;
+      const float* lse2s = stats + buf * 2 * BM;
+      const float* Ds = lse2s + BM;
+      // one 32-row query block at a time keeps the live registers of a block
+      // (its S, dP and operands) from being doubled by interleaving
+#pragma unroll 1
       for (int nb = 0; nb < BM / 32; ++nb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        bf16x8 qa[KC], da[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const bf16x8 qa = load_bf16x8(&Qs[(32 * nb + ln) * L::RS + 16 * kc + 8 * g]);
-          const bf16x8 da = load_bf16x8(&dOs[(32 * nb + ln) * L::RS + 16 * kc + 8 * g]);
-          s = mfma32(qa, kreg[kc], s);
-          dp = mfma32(da, vreg[kc], dp);
+          qa[kc] = load_bf16x8(&Qs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
+          da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
+        }
+        f32x16 s[NCB], dp[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          s[cb] = f32x16{};
+          dp[cb] = f32x16{};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            s[cb] = mfma32(qa[kc], kreg[cb][kc], s[cb]);
+            dp[cb] = mfma32(da[kc], vreg[cb][kc], dp[cb]);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -202,106 +199,276 @@ __global__ __launch_bounds__(bwdk::NT) void bwd_bf16_kernel(BwdArgs a) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[qi]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = kvalid ? fast_exp2(s[4 * i + r] * sl2 - l4[r]) : 0.f;
-            s[4 * i + r] = p;
-            dp[4 * i + r] = p * (dp[4 * i + r] - d4[r]);
-          }
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = fast_exp2(fmaf(s[cb][4 * i + r], sl2, -l4[r]));
+              s[cb][4 * i + r] = p;
+              dp[cb][4 * i + r] = p * (dp[cb][4 * i + r] - d4[r]);
+            }
         }
-        // dV += P^T dO, dK += dS^T Q over two 16-query chunks
+        // dV += P^T dO, dK += dS^T Q over two 16-query chunks t = 2 nb + hh:
+        // slot group g holds queries 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int t = 2 * nb + hh;
-          const bf16x8 pa = acc_half_to_bf16(s, hh);
-          const bf16x8 sa = acc_half_to_bf16(dp, hh);
+          bf16x8 pa[NCB], sa[NCB];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            pa[cb] = acc_half_to_bf16(s[cb], hh);
+            sa[cb] = acc_half_to_bf16(dp[cb], hh);
+          }
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const bf16* dr = &dOt[(32 * db + ln) * L::TS + 16 * t + 4 * g];
-            const bf16* qr = &Qt[(32 * db + ln) * L::TS + 16 * t + 4 * g];
-            const bf16x8 db8 = cat4(*reinterpret_cast<const bf16x4*>(dr),
-                                    *reinterpret_cast<const bf16x4*>(dr + 8));
-            const bf16x8 qb8 = cat4(*reinterpret_cast<const bf16x4*>(qr),
-                                    *reinterpret_cast<const bf16x4*>(qr + 8));
-            dv[db] = mfma32(pa, db8, dv[db]);
-            dk[db] = mfma32(sa, qb8, dk[db]);
+            const bf16x8 dob = tr_operand(dOs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+            const bf16x8 qbv = tr_operand(Qs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              if constexpr (kPinAcc) {
+                mfma32_agpr(pa[cb], dob, dv[cb][db]);
+                mfma32_agpr(sa[cb], qbv, dk[cb][db]);
+              } else {
+                dv[cb][db] = mfma32(pa[cb], dob, dv[cb][db]);
+                dk[cb][db] = mfma32(sa[cb], qbv, dk[cb][db]);
+              }
+            }
           }
         }
-        // dS to LDS as [query][key] for the dQ product
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qi = 32 * nb + 8 * (e >> 2) + 4 * g + (e & 3);
-          dSs[qi * L::SS + 32 * w + ln] = (bf16)dp[e];
-        }
-      }
-    } else {
-      // keys past Nkv: this wave's share of dS is zero
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int qi = 8 * (e >> 2) + 4 * g + (e & 3);
-        dSs[qi * L::SS + 32 * w + ln] = (bf16)0.f;
       }
     }
+    if (it + 1 < nqt) store_tile(buf ^ 1);
     __syncthreads();
-
-    // dQ tile (BM x D) = dS (BM x 128) K (128 x D), split over the waves in
-    // 32x32 blocks; atomically added to the fp32 accumulator.
-    for (int blk = w; blk < (BM / 32) * NDB; blk += 4) {
-      const int qbk = blk / NDB, db = blk % NDB;
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int t = 0; t < BN / 16; ++t) {
-        const bf16x8 sa = load_bf16x8(&dSs[(32 * qbk + ln) * L::SS + 16 * t + 8 * g]);
-        const bf16x8 kb8 = load_bf16x8(&Kt[(32 * db + ln) * L::KTS + 16 * t + 8 * g]);
-        acc = mfma32(sa, kb8, acc);
-      }
-      const int dcol = 32 * db + ln;
-      if (dcol < D) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qi = q0 + 32 * qbk + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (qi < a.Nq)
-            __hip_atomic_fetch_add(dqp + (int64_t)qi * a.dqa.sn + dcol, acc[e] * a.scale,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
   }
 
   if (!wave_active) return;
+  if constexpr (kPinAcc) agpr_results_ready();
   // dK (scaled) and dV: lane owns column d = 32db + ln, key rows 8i+4g+r
   bf16* dkp = (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh;
   bf16* dvp = (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int dcol = 32 * db + ln;
-    if (dcol >= D) continue;
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kr = kw + 8 * (e >> 2) + 4 * g + (e & 3);
-      if (kr < a.Nkv) {
-        dkp[(int64_t)kr * a.dks.sn + dcol] = (bf16)(dk[db][e] * a.scale);
-        dvp[(int64_t)kr * a.dvs.sn + dcol] = (bf16)dv[db][e];
+    for (int db = 0; db < NDB; ++db) {
+      const int dcol = 32 * db + ln;
+      if (dcol >= D) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kr = kw + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (kr < a.Nkv) {
+          dkp[(int64_t)kr * a.dks.sn + dcol] = (bf16)(dk[cb][db][e] * a.scale);
+          dvp[(int64_t)kr * a.dvs.sn + dcol] = (bf16)dv[cb][db][e];
+        }
       }
     }
-  }
 }
 
-// dQ accumulator (fp32) -> dQ (bf16), one thread per 4 elements
-__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdArgs a, int d) {
-  const int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int dq4 = d / 4;
-  const int64_t n4 = (int64_t)a.B * a.H * a.Nq * dq4;
-  if (e4 >= n4) return;
-  const int c = (int)(e4 % dq4) * 4;
-  const int64_t row = e4 / dq4;
-  const int i = (int)(row % a.Nq);
-  const int64_t bh = row / a.Nq;
-  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const f32x4 v = *reinterpret_cast<const f32x4*>(a.dq_acc + b * a.dqa.sb + h * a.dqa.sh +
-                                                  (int64_t)i * a.dqa.sn + c);
-  bf16x4 o4 = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-  *reinterpret_cast<bf16x4*>((bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)i * a.dqs.sn +
-                             c) = o4;
+// --------------------------------------------------------------------------
+// bf16 dQ kernel, query-outer.
+//
+// Same shape as the forward: 4 waves, each owning QW query rows; key/value
+// tiles of 64 rows stream through LDS (row-major, double-buffered).  Per tile
+// each wave recomputes the transposed tiles S^T = K Q^T and dP^T = V dO^T, so
+// every lane owns one query row (its LSE and D are per-lane scalars), forms
+// dS = P (dP - D), and accumulates dQ = dS K in registers: the accumulator
+// halves are the A operand and the K columns come from LDS transpose reads.
+// Each dQ row belongs to one workgroup, so no atomics are needed and the
+// result is bitwise reproducible.  Key rows past Nkv are zero in LDS and add
+// nothing (their K rows multiply dS).
+// --------------------------------------------------------------------------
+namespace dqk {
+constexpr int BN = 64;
+constexpr int NT = 256;
+}  // namespace dqk
+
+template <int D>
+struct DqLds {
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int KS = DP + 8;
+  static constexpr int tile = dqk::BN * KS;
+  static constexpr int bytes = 4 * tile * 2;   // K, V x double buffer
+};
+
+template <int D, int QW>
+__device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
+  using namespace dqk;
+  using L = DqLds<D>;
+  constexpr int DP = L::DP, NDB = DP / 32, KC = D / 16, KS = L::KS;
+  constexpr int NQB = QW / 32;
+  constexpr int BM = 4 * QW;
+  constexpr int CH = BN * (D / 8);
+  constexpr int PT = (CH + NT - 1) / NT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* const lds = reinterpret_cast<bf16*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ln = lane & 31, g = lane >> 5;
+
+  const int nqb = (a.Nq + BM - 1) / BM;
+  int idx = xcd_remap(blockIdx.x, gridDim.x);
+  const int qblk = idx % nqb;
+  idx /= nqb;
+  const int h = idx % a.H;
+  const int b = idx / a.H;
+
+  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
+  const bf16* dop = (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh;
+  const float* lsep = a.lse + ((int64_t)b * a.H + h) * a.Nq;
+  const float* dsp = a.dsum + ((int64_t)b * a.H + h) * a.Nq;
+
+  const int q0 = qblk * BM + w * QW;
+  const bool wave_active = q0 < a.Nq;
+  const bf16x8 zero8 = {};
+
+  bf16x8 qreg[NQB][KC], doreg[NQB][KC];
+  float lse2[NQB], dsum[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qrow = q0 + 32 * qb + ln;
+    const bool ok = qrow < a.Nq;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qreg[qb][kc] = ok ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g) : zero8;
+      doreg[qb][kc] = ok ? load_bf16x8(dop + (int64_t)qrow * a.dos.sn + 16 * kc + 8 * g) : zero8;
+    }
+    lse2[qb] = ok ? lsep[qrow] * kLog2e : INFINITY;
+    dsum[qb] = ok ? dsp[qrow] : 0.f;
+  }
+
+  const int n_kv = a.Nkv;
+  const int ntiles = (n_kv + BN - 1) / BN;
+  bf16x8 pk[PT], pv[PT];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      const int r = e / (D / 8), cc = e % (D / 8);
+      const bool ok = e < CH && j0 + r < n_kv;
+      pk[u] = ok ? load_bf16x8(kp + (int64_t)(j0 + r) * a.ks.sn + 8 * cc) : zero8;
+      pv[u] = ok ? load_bf16x8(vp + (int64_t)(j0 + r) * a.vs.sn + 8 * cc) : zero8;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    bf16* Kt = lds + buf * 2 * L::tile;
+    bf16* Vt = Kt + L::tile;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      if (e < CH) {
+        const int r = e / (D / 8), cc = e % (D / 8);
+        *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[u];
+        *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[u];
+      }
+    }
+  };
+
+  f32x16 dq[NQB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[qb][db] = f32x16{};
+  const float sl2 = a.scale * kLog2e;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) load_tile((it + 1) * BN);
+    if (wave_active) {
+      const bf16* Kt = lds + buf * 2 * L::tile;
+      const bf16* Vt = Kt + L::tile;
+      f32x16 st[2][NQB], dpt[2][NQB];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          st[cb][qb] = f32x16{};
+          dpt[cb][qb] = f32x16{};
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+          const bf16x8 va = load_bf16x8(&Vt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            st[cb][qb] = mfma32(ka, qreg[qb][kc], st[cb][qb]);
+            dpt[cb][qb] = mfma32(va, doreg[qb][kc], dpt[cb][qb]);
+          }
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(fmaf(st[cb][qb][e], sl2, -lse2[qb]));
+            st[cb][qb][e] = p * (dpt[cb][qb][e] - dsum[qb]);
+          }
+      // dQ += dS K over four 16-key chunks (slot group g: keys 16t + 4g +
+      // (0..3) and 16t + 8 + 4g + (0..3) = accumulator entries 8hh..8hh+7)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 sa[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) sa[qb] = acc_half_to_bf16(st[t >> 1][qb], t & 1);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 kb8 = tr_operand(Kt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) dq[qb][db] = mfma32(sa[qb], kb8, dq[qb][db]);
+        }
+      }
+    }
+    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int dcol = 32 * db + ln;
+      if (dcol >= D) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (qr >= a.Nq) continue;
+        const float v = dq[qb][db][e] * a.scale;
+        if (accumulate) {
+          float* p = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)qr * a.dqs.sn + dcol;
+          *p += v;
+        } else {
+          bf16* p = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)qr * a.dqs.sn + dcol;
+          *p = (bf16)v;
+        }
+      }
+    }
+}
+
+// Occupancy: kernels whose registers fit request two waves per SIMD.
+#ifndef EXATTN_DKDV_WAVES
+#define EXATTN_DKDV_WAVES 2
+#endif
+template <int D, int KW>
+__global__ __launch_bounds__(bwdk::NT)
+__attribute__((amdgpu_waves_per_eu(KW == 32 && D <= 80 ? EXATTN_DKDV_WAVES : 1)))
+void dkdv_bf16_kernel(BwdArgs a) {
+  dkdv_body<D, KW>(a);
+}
+template <int D, int QW>
+__global__ __launch_bounds__(dqk::NT) void dq_bf16_kernel(BwdArgs a, int accumulate) {
+  dq_body<D, QW>(a, accumulate);
+}
+template <int D, int QW>
+__global__ __launch_bounds__(dqk::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_bf16_kernel_w2(BwdArgs a, int accumulate) {
+  dq_body<D, QW>(a, accumulate);
 }
 
 // --------------------------------------------------------------------------
@@ -445,11 +612,18 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dq_kernel(BwdArgs a, int acc
 // --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
-static hipError_t launch_pre(const BwdArgs& a, int d, int is_bf16, hipStream_t s) {
+#ifndef EXATTN_DKDV_KW64
+#define EXATTN_DKDV_KW64 32
+#endif
+#ifndef EXATTN_DQ_QW64
+#define EXATTN_DQ_QW64 32
+#endif
+
+hipError_t launch_bwd_pre(const BwdArgs& a, int d, int in_bf16, hipStream_t s) {
   const long long rows = (long long)a.B * a.H * a.Nq;
   const long long grid = (rows + 15) / 16;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (is_bf16) {
+  if (in_bf16) {
     if (a.o_f32)
       hipLaunchKernelGGL((bwd_pre_kernel<bf16, float>), dim3((unsigned)grid), dim3(256), 0, s, a, d);
     else
@@ -460,54 +634,91 @@ static hipError_t launch_pre(const BwdArgs& a, int d, int is_bf16, hipStream_t s
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t bwd_bf16_d(const BwdArgs& a, int finalize_dq, hipStream_t s) {
-  hipError_t e = launch_pre(a, D, 1, s);
-  if (e != hipSuccess) return e;
-  const int nkb = (a.Nkv + bwdk::BN - 1) / bwdk::BN;
-  const long long grid = (long long)nkb * a.H * a.B;
+template <typename K>
+static hipError_t allow_lds(K kernel, int bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D, int KW>
+static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t s) {
+  const long long grid = (long long)((a.Nkv + 4 * KW - 1) / (4 * KW)) * a.H * a.B;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int lds = BwdLds<D>::bytes;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&bwd_bf16_kernel<D>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const int lds = DkdvLds<D>::bytes;
+  static const hipError_t attr = allow_lds(&dkdv_bf16_kernel<D, KW>, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((bwd_bf16_kernel<D>), dim3((unsigned)grid), dim3(bwdk::NT), lds, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess || !finalize_dq) return e;
-  const long long n4 = (long long)a.B * a.H * a.Nq * (D / 4);
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a, D);
+  hipLaunchKernelGGL((dkdv_bf16_kernel<D, KW>), dim3((unsigned)grid), dim3(bwdk::NT), lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int finalize_dq, hipStream_t s) {
+template <int D, int QW, bool W2>
+static hipError_t launch_dq(const BwdArgs& a, int accumulate, hipStream_t s) {
+  const long long grid = (long long)((a.Nq + 4 * QW - 1) / (4 * QW)) * a.H * a.B;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int lds = DqLds<D>::bytes;
+  if constexpr (W2) {
+    static const hipError_t attr = allow_lds(&dq_bf16_kernel_w2<D, QW>, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((dq_bf16_kernel_w2<D, QW>), dim3((unsigned)grid), dim3(dqk::NT), lds, s, a,
+                       accumulate);
+  } else {
+    static const hipError_t attr = allow_lds(&dq_bf16_kernel<D, QW>, lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((dq_bf16_kernel<D, QW>), dim3((unsigned)grid), dim3(dqk::NT), lds, s, a,
+                       accumulate);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int KW, int QW, bool W2>
+static hipError_t bwd_bf16_d(const BwdArgs& a, int do_dkdv, int do_dq, int accumulate,
+                             hipStream_t s) {
+  if (do_dkdv) {
+    const hipError_t e = launch_dkdv<D, KW>(a, s);
+    if (e != hipSuccess) return e;
+  }
+  if (do_dq) return launch_dq<D, QW, W2>(a, accumulate, s);
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
+                           hipStream_t s) {
   switch (d) {
-    case 64: return bwd_bf16_d<64>(a, finalize_dq, s);
-    case 80: return bwd_bf16_d<80>(a, finalize_dq, s);
-    case 128: return bwd_bf16_d<128>(a, finalize_dq, s);
+    case 64:
+      return bwd_bf16_d<64, EXATTN_DKDV_KW64, EXATTN_DQ_QW64, EXATTN_DQ_QW64 == 32>(
+          a, do_dkdv, do_dq, accumulate, s);
+    case 80: return bwd_bf16_d<80, 32, 32, true>(a, do_dkdv, do_dq, accumulate, s);
+    case 128: return bwd_bf16_d<128, 32, 32, false>(a, do_dkdv, do_dq, accumulate, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int D>
-static hipError_t bwd_f32_d(const BwdArgs& a, int accumulate, hipStream_t s) {
-  hipError_t e = launch_pre(a, D, 0, s);
-  if (e != hipSuccess) return e;
+static hipError_t bwd_f32_d(const BwdArgs& a, int do_dkdv, int do_dq, int accumulate,
+                            hipStream_t s) {
   const long long gk = (long long)((a.Nkv + bwdf::RB - 1) / bwdf::RB) * a.H * a.B;
   const long long gq = (long long)((a.Nq + bwdf::RB - 1) / bwdf::RB) * a.H * a.B;
   if (gk > 0x7fffffffLL || gq > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D>), dim3((unsigned)gk), dim3(bwdf::RB), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_f32_dq_kernel<D>), dim3((unsigned)gq), dim3(bwdf::RB), 0, s, a, accumulate);
-  return hipGetLastError();
+  if (do_dkdv) {
+    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D>), dim3((unsigned)gk), dim3(bwdf::RB), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (do_dq) {
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D>), dim3((unsigned)gq), dim3(bwdf::RB), 0, s, a,
+                       accumulate);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
-hipError_t launch_bwd_f32(const BwdArgs& a, int d, int accumulate, hipStream_t s) {
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
+                          hipStream_t s) {
   switch (d) {
-    case 64: return bwd_f32_d<64>(a, accumulate, s);
-    case 80: return bwd_f32_d<80>(a, accumulate, s);
-    case 128: return bwd_f32_d<128>(a, accumulate, s);
+    case 64: return bwd_f32_d<64>(a, do_dkdv, do_dq, accumulate, s);
+    case 80: return bwd_f32_d<80>(a, do_dkdv, do_dq, accumulate, s);
+    case 128: return bwd_f32_d<128>(a, do_dkdv, do_dq, accumulate, s);
   }
   return hipErrorInvalidValue;
 }

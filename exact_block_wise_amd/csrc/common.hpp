@@ -31,12 +31,80 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product with the accumulator pinned in AGPRs.  For accumulators
+// that only matrix instructions touch inside a loop (dK, dV), this keeps the
+// register allocator from parking them in AGPRs and copying them to VGPRs and
+// back around every product.  Chains of these on one accumulator need no
+// wait states (same shape, destination = srcC).  The compiler's hazard
+// tracking does not look inside inline assembly, so the leading s_nop covers
+// an accumulator the allocator may have just rewritten (v_accvgpr_write)
+// before the product reads it; kernels using this must still not spill.
+// Before VALU code reads the accumulator, call agpr_results_ready().
+__device__ __forceinline__ void mfma32_agpr(bf16x8 a, bf16x8 b, f32x16& c) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void agpr_results_ready() {
+  // covers the longest result latency of a 32x32 product (16 passes)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
-// value of the other half-wave (lane ^ 32)
+// value of the other half-wave (lane ^ 32), through the LDS crossbar
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: every lane sees
+// both halves' values, no LDS traffic)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// i receives element (i % 4) of the 8-byte pieces read by lanes
+// 4e + i / 4, e = 0..3.  So if lane j of the group reads row r(j / 4),
+// columns c0 + 4 (j % 4) .. +3 of a row-major tile, lane i receives column
+// c0 + i of rows r(0..3): a column of the tile, as a matrix-core operand.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4_t*)(const_cast<bf16*>(p)));
+}
+
+// Operand of a 32x32x16 product whose lane l must hold column (l % 32) of a
+// row-major LDS tile at 8 rows: rows rows_lo + (0..3) and rows_hi + (0..3),
+// where rows_lo / rows_hi already include this lane's slot group.  `tile`
+// points at element (0, c0) of the 32 columns; `ld` is the row stride.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ld, int rows_lo, int rows_hi,
+                                             int lane) {
+  const int i = lane & 15;
+  const int col = 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  const bf16x4 lo = lds_read_tr(tile + (rows_lo + (i >> 2)) * ld + col);
+  const bf16x4 hi = lds_read_tr(tile + (rows_hi + (i >> 2)) * ld + col);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum of the 8 bf16 values of an operand, accumulated in fp32 (v_dot2 with 1)
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);

@@ -10,41 +10,74 @@
 
 #include <math.h>
 
+// query rows per wave of the bf16 forward for d = 64 and d = 80
+#ifndef EXATTN_FWD_QW64
+#define EXATTN_FWD_QW64 32
+#endif
+#ifndef EXATTN_FWD_QW80
+#define EXATTN_FWD_QW80 32
+#endif
+// occupancy request (waves per SIMD) of the bf16 forward for d = 64;
+// d = 80 and 128 ask for two (three would spill)
+#ifndef EXATTN_FWD_WAVES
+#define EXATTN_FWD_WAVES 3
+#endif
+
 namespace exattn {
 
 // --------------------------------------------------------------------------
 // bf16 inputs, bf16 matrix cores (32x32x16), fp32 accumulation.
 //
-// Workgroup: 4 waves, 128 query rows (32 per wave).  Key/value tiles of 64
-// rows are staged in LDS: K row-major, V transposed.  Each wave computes the
-// transposed score tile S^T = K Q^T so that every lane owns one query row
-// (column n = lane % 32 of the accumulator): the softmax statistics are then
-// per-lane scalars, and the exponentiated tile is already laid out as the B
-// operand of O^T += V^T P^T.
+// Workgroup: 4 waves, each owning QW query rows (QW = 32 or 64).  Key/value
+// tiles of 64 rows are staged in LDS row-major and double-buffered: the next
+// tile's global loads are issued into registers before the current tile is
+// computed and written to the other buffer after it, so one barrier per tile
+// suffices and the load latency hides behind the matrix work.
+//
+// Each wave computes the transposed score tile S^T = K Q^T: every lane then
+// owns one query row (accumulator column lane % 32), the softmax statistics
+// are per-lane scalars, and the exponentiated tile is already in the B-operand
+// layout of O^T += V^T P^T.  The V^T operand is read straight from the
+// row-major V tile with LDS transpose reads.
+//
+// The running maximum is refreshed lazily: the reference value m used in
+// exp2(s - m) is raised only when a row's maximum exceeds it by more than
+// 2^8 in the exponent, which bounds the weights by 256; any reference value
+// gives the same O and LSE, so this changes rounding only.
 // --------------------------------------------------------------------------
 namespace fwdk {
-constexpr int BM = 128;
 constexpr int BN = 64;
 constexpr int NT = 256;
+constexpr float kLazy = 8.0f;  // log2 of the largest weight allowed before rescaling
 }  // namespace fwdk
 
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(fwdk::NT) void fwd_bf16_kernel(FwdArgs a) {
+template <int D>
+struct FwdLds {
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int KS = DP + 8;                // row stride of the K and V tiles
+  static constexpr int tile = fwdk::BN * KS;        // elements per tile
+  static constexpr int bytes = 4 * tile * 2;        // K, V x double buffer
+};
+
+template <int D, int QW, bool OUT_F32>
+__global__ __launch_bounds__(fwdk::NT)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? EXATTN_FWD_WAVES : 2)))
+void fwd_bf16_kernel(FwdArgs a) {
   using namespace fwdk;
-  constexpr int DP = (D + 31) / 32 * 32;  // output rows in 32-row blocks
-  constexpr int NDB = DP / 32;
-  constexpr int KC = D / 16;              // contraction chunks of QK^T
-  constexpr int KS = D + 8;               // K tile row stride (elements)
-  constexpr int VS = BN + 4;              // V^T tile row stride (elements)
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[DP * VS];
+  using L = FwdLds<D>;
+  constexpr int DP = L::DP, NDB = DP / 32, KC = D / 16, KS = L::KS;
+  constexpr int NQB = QW / 32;          // 32-row query blocks per wave
+  constexpr int BM = 4 * QW;            // query rows per workgroup
+  constexpr int CH = BN * (D / 8);      // 16-byte pieces per tile
+  constexpr int PT = (CH + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) bf16 lds[4 * L::tile];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ln = lane & 31, g = lane >> 5;
 
   const int nqb = (a.Nq + BM - 1) / BM;
   int idx = xcd_remap(blockIdx.x, gridDim.x);
-  const int qb = idx % nqb;
+  const int qblk = idx % nqb;
   idx /= nqb;
   const int h = idx % a.H;
   idx /= a.H;
@@ -52,143 +85,198 @@ __global__ __launch_bounds__(fwdk::NT) void fwd_bf16_kernel(FwdArgs a) {
   const int c = idx / a.B;
 
   const int kv_lo = c * a.chunk_len;
-  const int kv_hi = min(a.Nkv, kv_lo + a.chunk_len);
-  const int n_kv = max(0, kv_hi - kv_lo);
+  const int n_kv = max(0, min(a.Nkv, kv_lo + a.chunk_len) - kv_lo);
+  const int ntiles = (n_kv + BN - 1) / BN;
 
   const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
   const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh + (int64_t)kv_lo * a.ks.sn;
   const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh + (int64_t)kv_lo * a.vs.sn;
 
-  const int q0 = qb * BM + w * 32;
+  const int q0 = qblk * BM + w * QW;
   const bool wave_active = q0 < a.Nq;
-  const int qrow = q0 + ln;
-  const bool qvalid = qrow < a.Nq;
-
-  // Padding rows of V^T (D <= d < DP) feed only discarded output rows; clear
-  // them once so they hold finite values.
-  if constexpr (DP != D) {
-    for (int i = tid; i < (DP - D) * VS; i += NT) Vt[D * VS + i] = (bf16)0.f;
-  }
-
-  bf16x8 qreg[KC];
   const bf16x8 zero8 = {};
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    qreg[kc] = qvalid ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g) : zero8;
 
-  f32x16 oacc[NDB];
+  // this wave's query rows as B operands: lane -> row q0 + 32 qb + ln,
+  // d = 16 kc + 8 g .. +7
+  bf16x8 qreg[NQB][KC];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  float m = -INFINITY;  // running max of the log2-scaled scores
-  float l = 0.f;        // this lane's share of the running sum
-  const float sl2 = a.scale * kLog2e;
-
-  for (int j0 = 0; j0 < n_kv; j0 += BN) {
-    __syncthreads();
-    // K tile, row-major: consecutive threads read consecutive 16-byte pieces
-    // of a row.
-    for (int e = tid; e < BN * (D / 8); e += NT) {
-      const int r = e / (D / 8), cc = e % (D / 8);
-      bf16x8 val = zero8;
-      if (j0 + r < n_kv) val = load_bf16x8(kp + (int64_t)(j0 + r) * a.ks.sn + 8 * cc);
-      *reinterpret_cast<bf16x8*>(&Ks[r * KS + 8 * cc]) = val;
-    }
-    // V tile, transposed: consecutive threads take consecutive rows so the
-    // 2-byte LDS writes of one instruction fall in distinct banks.
-    for (int e = tid; e < BN * (D / 8); e += NT) {
-      const int r = e % BN, cc = e / BN;
-      bf16x8 val = zero8;
-      if (j0 + r < n_kv) val = load_bf16x8(vp + (int64_t)(j0 + r) * a.vs.sn + 8 * cc);
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qrow = q0 + 32 * qb + ln;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) Vt[(8 * cc + i) * VS + r] = val[i];
-    }
-    __syncthreads();
-    if (!wave_active) continue;
-
-    // S^T (two 32-row key blocks) = K Q^T
-    f32x16 s[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      s[cb] = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8 ka = load_bf16x8(&Ks[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
-        s[cb] = mfma32(ka, qreg[kc], s[cb]);
-      }
-    }
-    // scale to log2 units, mask the ragged tail, row maximum
-    float mx = -INFINITY;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kv = j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3);
-        const float x = kv < n_kv ? s[cb][e] * sl2 : -INFINITY;
-        s[cb][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
-    float rs = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(s[cb][e] - m_new);
-        s[cb][e] = p;
-        rs += p;
-      }
-    }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-
-    // O^T += V^T P^T over four 16-key chunks.  Chunk t = 2*cb + hh holds,
-    // for group g, keys 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3): the
-    // accumulator entries 8hh .. 8hh+7 of key block cb.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 pb = acc_half_to_bf16(s[t >> 1], t & 1);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16* vr = &Vt[(32 * db + ln) * VS + 16 * t + 4 * g];
-        const bf16x8 va = cat4(*reinterpret_cast<const bf16x4*>(vr),
-                               *reinterpret_cast<const bf16x4*>(vr + 8));
-        oacc[db] = mfma32(va, pb, oacc[db]);
-      }
-    }
+    for (int kc = 0; kc < KC; ++kc)
+      qreg[qb][kc] = qrow < a.Nq ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g)
+                                 : zero8;
   }
 
-  if (!wave_active) return;
-  l += xor32(l);
-  if (!qvalid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int64_t orow = (int64_t)c * a.o_chunk_stride + b * a.os.sb + h * a.os.sh +
-                       (int64_t)qrow * a.os.sn;
+  // tile loader: piece e -> row e / (D/8), 16-byte column piece e % (D/8)
+  bf16x8 pk[PT], pv[PT];
+  auto load_tile = [&](int j0) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      const int r = e / (D / 8), cc = e % (D / 8);
+      const bool ok = e < CH && j0 + r < n_kv;
+      pk[u] = ok ? load_bf16x8(kp + (int64_t)(j0 + r) * a.ks.sn + 8 * cc) : zero8;
+      pv[u] = ok ? load_bf16x8(vp + (int64_t)(j0 + r) * a.vs.sn + 8 * cc) : zero8;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    bf16* Kt = lds + buf * 2 * L::tile;
+    bf16* Vt = Kt + L::tile;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = 32 * db + 8 * i + 4 * g;
-      if (d0 < D) {
-        if constexpr (OUT_F32) {
-          f32x4 v4 = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv,
-                      oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv};
-          *reinterpret_cast<f32x4*>((float*)a.o + orow + d0) = v4;
-        } else {
-          bf16x4 v4 = {(bf16)(oacc[db][4 * i] * inv), (bf16)(oacc[db][4 * i + 1] * inv),
-                       (bf16)(oacc[db][4 * i + 2] * inv), (bf16)(oacc[db][4 * i + 3] * inv)};
-          *reinterpret_cast<bf16x4*>((bf16*)a.o + orow + d0) = v4;
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      if (e < CH) {
+        const int r = e / (D / 8), cc = e % (D / 8);
+        *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[u];
+        *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[u];
+      }
+    }
+  };
+
+  f32x16 oacc[NDB][NQB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = f32x16{};
+  float mref[NQB], lsum[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    mref[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+  }
+  const float sl2 = a.scale * kLog2e;
+  const float lazy = kLazy / sl2;  // threshold in raw score units
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = it * BN;
+    const int buf = it & 1;
+    if (it + 1 < ntiles) load_tile(j0 + BN);
+    if (wave_active) {
+      const bf16* Kt = lds + buf * 2 * L::tile;
+      const bf16* Vt = Kt + L::tile;
+      // S^T = K Q^T for two 32-key blocks x NQB query blocks
+      f32x16 s[2][NQB];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
+        }
+      }
+      if (j0 + BN > n_kv) {  // ragged last tile: keys past the end weigh nothing
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const bool dead = j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3) >= n_kv;
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              if (dead) s[cb][qb][e] = -INFINITY;
+          }
+      }
+      // row maxima; raise the reference only when it is exceeded by > 2^8
+      bool raise = false;
+      float mx[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float m = s[0][qb][0];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = fmaxf(m, s[cb][qb][e]);
+        mx[qb] = max_halves(m);
+        raise |= mx[qb] > mref[qb] + lazy;
+      }
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float mnew = fmaxf(mref[qb], mx[qb]);
+          const float alpha = fast_exp2((mref[qb] - mnew) * sl2);
+          mref[qb] = mnew;
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
+        }
+      }
+      // P = exp2(sl2 (s - mref)), then O^T += V^T P^T over four 16-key chunks.
+      // Chunk t = 2 cb + hh holds, for slot group g, keys 16t + 4g + (0..3)
+      // and 16t + 8 + 4g + (0..3): accumulator entries 8hh .. 8hh+7 of block cb.
+      bf16x8 pb[4][NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float moff = mref[qb] * sl2;
+        // the row sum is taken over the fp32 weights: a peaky row's few
+        // dominant weights would carry their bf16 rounding into the LSE
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(fmaf(s[cb][qb][e], sl2, -moff));
+            s[cb][qb][e] = p;
+            part[e & 3] += p;
+          }
+        lsum[qb] += (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pb[t][qb] = acc_half_to_bf16(s[t >> 1][qb], t & 1);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = mfma32(va, pb[t][qb], oacc[db][qb]);
         }
       }
     }
+    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
   }
-  if (g == 0) {
-    const int64_t li = (int64_t)c * a.lse_chunk_stride + ((int64_t)b * a.H + h) * a.Nq + qrow;
-    a.lse[li] = l > 0.f ? m * kLn2 + logf(l) : -INFINITY;
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float l = sum_halves(lsum[qb]);
+    const int qrow = q0 + 32 * qb + ln;
+    if (qrow >= a.Nq) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t orow = (int64_t)c * a.o_chunk_stride + b * a.os.sb + h * a.os.sh +
+                         (int64_t)qrow * a.os.sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * g;
+        if (d0 < D) {
+          const f32x16& o = oacc[db][qb];
+          if constexpr (OUT_F32) {
+            f32x4 v4 = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv,
+                        o[4 * i + 3] * inv};
+            *reinterpret_cast<f32x4*>((float*)a.o + orow + d0) = v4;
+          } else {
+            bf16x4 v4 = {(bf16)(o[4 * i] * inv), (bf16)(o[4 * i + 1] * inv),
+                         (bf16)(o[4 * i + 2] * inv), (bf16)(o[4 * i + 3] * inv)};
+            *reinterpret_cast<bf16x4*>((bf16*)a.o + orow + d0) = v4;
+          }
+        }
+      }
+    }
+    if (g == 0) {
+      const int64_t li = (int64_t)c * a.lse_chunk_stride + ((int64_t)b * a.H + h) * a.Nq + qrow;
+      a.lse[li] = l > 0.f ? (mref[qb] * sl2 + log2f(l)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -274,23 +362,25 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   a.lse[li] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-template <int D>
+template <int D, int QW>
 static hipError_t fwd_bf16_d(const FwdArgs& a, hipStream_t s) {
-  const int nqb = (a.Nq + fwdk::BM - 1) / fwdk::BM;
+  const int nqb = (a.Nq + 4 * QW - 1) / (4 * QW);
   const long long grid = (long long)nqb * a.H * a.B * a.n_chunks;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.out_f32)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3((unsigned)grid), dim3(fwdk::NT), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QW, true>), dim3((unsigned)grid), dim3(fwdk::NT), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3((unsigned)grid), dim3(fwdk::NT), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QW, false>), dim3((unsigned)grid), dim3(fwdk::NT), 0,
+                       s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
   switch (d) {
-    case 64: return fwd_bf16_d<64>(a, s);
-    case 80: return fwd_bf16_d<80>(a, s);
-    case 128: return fwd_bf16_d<128>(a, s);
+    case 64: return fwd_bf16_d<64, EXATTN_FWD_QW64>(a, s);
+    case 80: return fwd_bf16_d<80, EXATTN_FWD_QW80>(a, s);
+    case 128: return fwd_bf16_d<128, 32>(a, s);
   }
   return hipErrorInvalidValue;
 }

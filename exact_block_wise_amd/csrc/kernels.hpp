@@ -34,16 +34,14 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  void* dq;      // final dQ (input dtype), or the fp32 accumulator target
+  void* dq;      // dQ: input dtype, or fp32 when accumulating
   void* dk;
   void* dv;
-  float* dsum;   // [B,H,Nq] workspace: D_i = dO_i . O_i
-  float* dq_acc; // fp32 accumulator, strides dqa
-  Strides qs, ks, vs, os, dos, dqs, dks, dvs, dqa;
+  float* dsum;   // [B,H,Nq] contiguous: D_i = dO_i . O_i
+  Strides qs, ks, vs, os, dos, dqs, dks, dvs;
   int B, H, Nq, Nkv;
   float scale;
-  int o_f32;       // o dtype is fp32
-  int zero_dq_acc; // preprocess clears dq_acc
+  int o_f32;     // o dtype is fp32
 };
 
 struct MergeArgs {
@@ -58,8 +56,11 @@ struct MergeArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int finalize_dq, hipStream_t s);
-hipError_t launch_bwd_f32(const BwdArgs& a, int d, int accumulate, hipStream_t s);
+hipError_t launch_bwd_pre(const BwdArgs& a, int d, int in_bf16, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
+                           hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
+                          hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace exattn

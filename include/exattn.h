@@ -75,10 +75,21 @@ typedef struct {
   float scale;
 } attn_problem;
 
-/* attn_bwd flag: dq is F32 and the gradient is ADDED to it.  Used for the
- * backward over key/value chunks, where dQ is the sum of the chunks'
- * contributions. */
+/* attn_bwd flags.
+ * DQ_ACCUMULATE: dq is F32 and the gradient is ADDED to it.  Used for the
+ *   backward over key/value chunks, where dQ is the sum of the chunks'
+ *   contributions.
+ * D_PRECOMPUTED: the workspace already holds D = rowsum(dO * O) for these o
+ *   and dout (from attn_bwd_preprocess, or an earlier attn_bwd call with the
+ *   same o, dout and workspace); the preprocess is skipped and o may be NULL.
+ *   Lets the chunks of a chunked backward share one preprocess.
+ * NO_DQ / NO_DKDV: skip dQ (dq may be NULL) or dK and dV (dk, dv may be
+ *   NULL).  The two halves are independent given D, so a caller may run them
+ *   on two streams. */
 #define ATTN_BWD_DQ_ACCUMULATE 1u
+#define ATTN_BWD_D_PRECOMPUTED 2u
+#define ATTN_BWD_NO_DQ 4u
+#define ATTN_BWD_NO_DKDV 8u
 
 /*
  * attn_fwd -- forward pass: O and the per-row log-sum-exp.
@@ -141,10 +152,23 @@ attn_status attn_lse_merge(int32_t n_parts, int32_t B, int32_t H, int32_t Nq,
 
 /*
  * attn_bwd_workspace_bytes -- device workspace attn_bwd needs for problem p
- * and the given flags (0 if p is invalid).  The caller allocates it; its
- * contents on entry do not matter.
+ * and the given flags (0 if p is invalid): B*H*Nq floats for D, rounded up
+ * to 256 bytes.  The caller allocates it; unless ATTN_BWD_D_PRECOMPUTED is
+ * passed its contents on entry do not matter.
  */
 size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags);
+
+/*
+ * attn_bwd_preprocess -- D_i = sum_c dO_ic O_ic, the per-row term of the
+ * softmax Jacobian (equal to sum_j P_ij dP_ij for the full row), in fp32.
+ *
+ *   o [B,H,Nq,d] (F32 or BF16), dout [B,H,Nq,d] (F32 or BF16).  Read only.
+ *   dsum [B,H,Nq] fp32 contiguous, 4-byte aligned.  Written.  Passing the
+ *      attn_bwd workspace here and ATTN_BWD_D_PRECOMPUTED to attn_bwd skips
+ *      attn_bwd's own preprocess.
+ */
+attn_status attn_bwd_preprocess(const attn_problem* p, attn_tensor o, attn_tensor dout,
+                                float* dsum, void* stream);
 
 /*
  * attn_bwd -- backward pass for the loss gradient dO, from the saved LSE.
@@ -155,6 +179,9 @@ size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags);
  *     P  = exp(scale Q K^T - LSE)
  *     dV = P^T dO,   dP = dO V^T,   D_i = dO_i . O_i,
  *     dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
+ * dK and dV are computed key-block by key-block and dQ query-block by
+ * query-block, each output row by exactly one workgroup: no atomics, and the
+ * results are bitwise reproducible.
  *
  *   q, k, v, dout: the forward's inputs and the output gradient, one dtype.
  *   o [B,H,Nq,d]: the forward output (F32 or BF16).  Only D = rowsum(dO*O)
@@ -166,9 +193,8 @@ size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags);
  *   dq [B,H,Nq,d], dk/dv [B,H,Nkv,d]: the input dtype, written; except dq
  *      under ATTN_BWD_DQ_ACCUMULATE, which must be F32 and is added to.
  *   workspace: device memory of at least attn_bwd_workspace_bytes(p, flags)
- *      bytes, 256-byte aligned; scratch for D and the fp32 dQ accumulator.
- * dQ is accumulated with fp32 atomics, so results are not bitwise
- * reproducible run to run; they are within rounding of the exact value.
+ *      bytes, 256-byte aligned: D = rowsum(dO * O) (see ATTN_BWD_D_PRECOMPUTED).
+ *   flags: ATTN_BWD_* above; passing both NO_DQ and NO_DKDV is invalid.
  */
 attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k,
                      attn_tensor v, attn_tensor o, attn_tensor dout,

@@ -34,8 +34,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "attn_abi_version", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd",
-        "attn_fwd_chunked", "attn_lse_merge", "attn_status_string"])
+        "attn_abi_version", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes",
+        "attn_fwd", "attn_fwd_chunked", "attn_lse_merge", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -112,8 +112,8 @@ def test_workspace_query(lib):
     p = P(B=32, H=12, Nq=1568, Nkv=1568, d=64)
     rows = 32 * 12 * 1568
     rup = lambda x: (x + 255) // 256 * 256
-    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 0) == rup(rows * 4) + rup(rows * 64 * 4)
-    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), 1) == rup(rows * 4)
+    for flags in (0, 1, 2, 4, 8):
+        assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), flags) == rup(rows * 4)
     assert lib.attn_bwd_workspace_bytes(None, 0) == 0
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(P(d=96)), 0) == 0
 
@@ -124,7 +124,8 @@ def bwd(lib, p=None, dq=None, flags=0, ws=FAKE, ws_bytes=1 << 40, o=None, dout=N
 
 
 def test_bwd_validation(lib):
-    assert bwd(lib, flags=2) == INVALID
+    assert bwd(lib, flags=16) == INVALID                 # unknown flag
+    assert bwd(lib, flags=4 | 8) == INVALID              # nothing to compute
     assert bwd(lib, lse=0) == INVALID
     assert bwd(lib, dout=T(dtype=0)) == INVALID
     assert bwd(lib, dq=T(dtype=1), flags=1) == INVALID   # accumulate needs an fp32 dq
@@ -134,3 +135,23 @@ def test_bwd_validation(lib):
     assert bwd(lib, ws=FAKE + 128) == WORKSPACE          # not 256-byte aligned
     assert bwd(lib, p=P(d=48)) == UNSUPPORTED
     assert bwd(lib, o=T(dtype=0), dq=T(dtype=0), flags=1, ws_bytes=0) == WORKSPACE
+
+
+def test_bwd_optional_outputs_validation(lib):
+    # with NO_DQ a null dq is allowed, so validation reaches the next check
+    null = T(ptr=0)
+    assert bwd(lib, dq=null, flags=4, ws=0) == WORKSPACE
+    assert bwd(lib, dq=null, flags=0) == INVALID
+    # with D_PRECOMPUTED a null o is allowed
+    assert bwd(lib, o=null, flags=2, ws=0) == WORKSPACE
+    assert bwd(lib, o=null, flags=0) == INVALID
+
+
+def test_preprocess_validation(lib):
+    def call(p=None, o=None, dout=None, dsum=FAKE):
+        return lib.attn_bwd_preprocess(ctypes.byref(p or P()), o or T(), dout or T(), dsum, None)
+    assert call(dsum=0) == INVALID
+    assert call(dsum=FAKE + 2) == UNSUPPORTED
+    assert call(o=T(ptr=0)) == INVALID
+    assert call(o=T(dtype=1), dout=T(dtype=0)) == INVALID   # f32 dO needs an f32 O
+    assert call(p=P(d=40)) == UNSUPPORTED
