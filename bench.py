@@ -23,6 +23,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import hashlib
+import glob
+import csv
+
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
@@ -36,7 +40,108 @@ def parse():
     ap.add_argument("--workload", default="vit_b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (for the HBM "
+                         "counter scale factors)")
+    ap.add_argument("--make-traffic-profile", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                    "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results of a bench run "
+                         "and of a --copy-calibration run into profiles/*_traffic.txt")
     return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, from hardware counters
+# --------------------------------------------------------------------------
+KERNEL_SOURCES = {"fwd": "fwd.hip", "fwd_chunked": "fwd.hip", "bwd_dkdv": "bwd.hip",
+                  "bwd_dq": "bwd.hip"}
+KERNEL_SYMBOLS = {"fwd": "fwd_", "fwd_chunked": "fwd_", "bwd_dkdv": "dkdv_bf16_kernel",
+                  "bwd_dq": "dq_bf16_kernel"}
+COPY_BYTES = 1 << 31  # 2 GiB read and 2 GiB written by the calibration copy
+
+
+def source_digest(call):
+    path = os.path.join(ROOT, "exact_block_wise_amd", "csrc", KERNEL_SOURCES[call])
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "exact_block_wise_amd", "csrc", "common.hpp")):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    """A plain copy of COPY_BYTES (read once, written once), repeated."""
+    import torch
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}))
+
+
+def _pmc_per_dispatch(d, counter, name_part):
+    """Mean per-dispatch value of `counter` (summed over instances) for the
+    kernels whose name contains name_part, from a rocprofv3 --pmc csv dir."""
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+                continue
+            key = (f, r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for '{name_part}' under {d}")
+    vals = sorted(per.values())
+    return vals[len(vals) // 2]
+
+
+def make_traffic_profile(dirs, workload):
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    cf = _pmc_per_dispatch(cfetch_dir, "FETCH_SIZE", "copy") * 1024 / COPY_BYTES
+    cw = _pmc_per_dispatch(cwrite_dir, "WRITE_SIZE", "copy") * 1024 / COPY_BYTES
+    lines = []
+    for call, sym in KERNEL_SYMBOLS.items():
+        try:
+            fk = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", sym)
+            wk = _pmc_per_dispatch(write_dir, "WRITE_SIZE", sym)
+        except SystemExit:
+            continue
+        traffic = fk * 1024 / cf + wk * 1024 / cw
+        lines.append(f"{call} source={source_digest(call)} fetch_kib={fk:.1f} write_kib={wk:.1f} "
+                     f"traffic_bytes={traffic:.0f}")
+    out = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
+    with open(out, "w") as f:
+        f.write(f"# HBM traffic per dispatch, workload {workload}, from rocprofv3 --pmc\n")
+        f.write("# commands (repo root, MI355X), each counter in its own run:\n")
+        f.write(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -- python bench.py "
+                f"--workload {workload} --steps 1 --warmup 1 --no-cpu-baseline\n")
+        f.write("#   (same with WRITE_SIZE into <W>)\n")
+        f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <CF> -- python bench.py "
+                "--copy-calibration   (and WRITE_SIZE into <CW>)\n")
+        f.write("#   python bench.py --workload %s --make-traffic-profile <F> <W> <CF> <CW>\n"
+                % workload)
+        f.write(f"# copy calibration: {COPY_BYTES} bytes read and written; counter/bytes "
+                f"factors fetch={cf:.4f} write={cw:.4f}\n")
+        f.write("# traffic_bytes = fetch_kib*1024/fetch_factor + write_kib*1024/write_factor;\n")
+        f.write("# source = digest of the kernel's source when measured (the bench reports the\n")
+        f.write("# traffic only while the source is unchanged)\n")
+        f.write(f"copy_fetch_factor={cf:.6f} copy_write_factor={cw:.6f}\n")
+        for ln in lines:
+            f.write(ln + "\n")
+    print(open(out).read())
+
+
+def measured_traffic(call, workload):
+    """traffic_bytes of `call` from profiles/, or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for ln in open(path):
+        if ln.startswith(call + " "):
+            kv = dict(x.split("=", 1) for x in ln.split()[1:])
+            if kv.get("source") == source_digest(call):
+                return int(float(kv["traffic_bytes"]))
+    return None
 
 
 def upload(w, torch):
@@ -89,6 +194,12 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.make_traffic_profile:
+        make_traffic_profile(args.make_traffic_profile, args.workload)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -176,11 +287,12 @@ def main():
         achieved = alg / (dom_t * 1e-3) / 1e9
         roof = {"kernel": dom[0], "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None}
+                "traffic": measured_traffic(dom[0], w.name)}
     else:
         achieved = dom[1] * u / (dom_t * 1e-3) / 1e12
         roof = {"kernel": dom[0], "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(dom[0], w.name)}
 
     line = {
         "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, video ViT-B N=1568",

@@ -1,7 +1,7 @@
 // C-ABI entry points: host-side validation, then kernel dispatch on the
 // caller's stream.  Nothing here allocates, copies, synchronises or keeps
 // mutable state; an argument error returns before any work is enqueued.
-#include "../../include/exattn.h"
+#include "exattn.h"
 
 #include <math.h>
 

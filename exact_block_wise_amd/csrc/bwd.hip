@@ -12,6 +12,15 @@
 #include <math.h>
 
 
+// pin the dK/dV accumulators of one-wave-per-SIMD instances in AGPRs
+#ifndef EXATTN_PIN_ACC
+#define EXATTN_PIN_ACC 1
+#endif
+// interleave two key blocks per wave (64 key rows) with scheduling hints
+#ifndef EXATTN_DKDV_PIPE
+#define EXATTN_DKDV_PIPE 0
+#endif
+
 namespace exattn {
 
 // --------------------------------------------------------------------------
@@ -74,7 +83,9 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   constexpr int NCB = KW / 32;                 // 32-row key blocks per wave
   // pin dK/dV in AGPRs only in the one-wave-per-SIMD instances, where the
   // registers fit without spilling (see mfma32_agpr)
-  constexpr bool kPinAcc = KW == 64 || D > 80;
+  constexpr bool kPinAcc = EXATTN_PIN_ACC && (KW == 64 || D > 80);
+  // explicit MFMA / VALU interleaving of two key blocks (builtin products)
+  constexpr bool kPipe = EXATTN_DKDV_PIPE && !kPinAcc;
   constexpr int BN = 4 * KW;                   // key rows per workgroup
   constexpr int CH = BM * (D / 8);             // 16-byte pieces per Q (or dO) tile
   constexpr int PT = (CH + NT - 1) / NT;
@@ -160,6 +171,93 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const float sl2 = a.scale * kLog2e;
   const int nqt = (a.Nq + BM - 1) / BM;
 
+  // Two key blocks per wave, arranged so that the matrix work of one block
+  // overlaps the elementwise work of the other inside the wave:
+  //   S/dP(cb0) | S/dP(cb1) + P,dS(cb0) | dV/dK(cb0) + P,dS(cb1) | dV/dK(cb1)
+  // The sched_group_barrier hints ask the scheduler to alternate one matrix
+  // instruction with a few vector instructions in the overlapped phases.
+  auto pipelined_block = [&](const bf16* Qs, const bf16* dOs, const float* lse2s,
+                             const float* Ds, int nb) {
+    bf16x8 qa[KC], da[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qa[kc] = load_bf16x8(&Qs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
+      da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
+    }
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = 32 * nb + 8 * i + 4 * g;
+      l4[i] = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
+      d4[i] = *reinterpret_cast<const f32x4*>(&Ds[qi]);
+    }
+    auto sdp = [&](int cb, f32x16& s_, f32x16& dp_) {
+      s_ = f32x16{};
+      dp_ = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        s_ = mfma32(qa[kc], kreg[cb][kc], s_);
+        dp_ = mfma32(da[kc], vreg[cb][kc], dp_);
+      }
+    };
+    auto elementwise = [&](f32x16& s_, f32x16& dp_) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(s_[4 * i + r], sl2, -l4[i][r]));
+          s_[4 * i + r] = p;
+          dp_[4 * i + r] = p * (dp_[4 * i + r] - d4[i][r]);
+        }
+    };
+    // transposed B operands (dO and Q columns) for both 16-query chunks
+    bf16x8 dob[2][NDB], qbv[2][NDB];
+    auto load_tr = [&]() {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int t = 2 * nb + hh;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dob[hh][db] = tr_operand(dOs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+          qbv[hh][db] = tr_operand(Qs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+        }
+      }
+    };
+    auto dvdk = [&](int cb, const f32x16& p_, const f32x16& ds_) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8 pa = acc_half_to_bf16(p_, hh);
+        const bf16x8 sa = acc_half_to_bf16(ds_, hh);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv[cb][db] = mfma32(pa, dob[hh][db], dv[cb][db]);
+          dk[cb][db] = mfma32(sa, qbv[hh][db], dk[cb][db]);
+        }
+      }
+    };
+    f32x16 s0, dp0, s1, dp1;
+    sdp(0, s0, dp0);
+    load_tr();
+    __builtin_amdgcn_sched_barrier(0);
+    sdp(1, s1, dp1);
+    elementwise(s0, dp0);
+#pragma unroll
+    for (int k = 0; k < 2 * KC; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix op
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight vector ops
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dvdk(0, s0, dp0);
+    elementwise(s1, dp1);
+#pragma unroll
+    for (int k = 0; k < 4 * NDB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dvdk(1, s1, dp1);
+  };
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -176,6 +274,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       // (its S, dP and operands) from being doubled by interleaving
 #pragma unroll 1
       for (int nb = 0; nb < BM / 32; ++nb) {
+        if constexpr (NCB == 2 && kPipe) {
+          pipelined_block(Qs, dOs, lse2s, Ds, nb);
+          continue;
+        }
         bf16x8 qa[KC], da[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -615,6 +717,7 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dq_kernel(BwdArgs a, int acc
 #ifndef EXATTN_DKDV_KW64
 #define EXATTN_DKDV_KW64 32
 #endif
+
 #ifndef EXATTN_DQ_QW64
 #define EXATTN_DQ_QW64 32
 #endif

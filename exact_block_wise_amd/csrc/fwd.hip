@@ -10,6 +10,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 // query rows per wave of the bf16 forward for d = 64 and d = 80
 #ifndef EXATTN_FWD_QW64
 #define EXATTN_FWD_QW64 32
@@ -17,10 +19,11 @@
 #ifndef EXATTN_FWD_QW80
 #define EXATTN_FWD_QW80 32
 #endif
-// occupancy request (waves per SIMD) of the bf16 forward for d = 64;
+// occupancy request (waves per SIMD) of the bf16 forward for d = 64 (its
+// registers then still fit three);
 // d = 80 and 128 ask for two (three would spill)
 #ifndef EXATTN_FWD_WAVES
-#define EXATTN_FWD_WAVES 3
+#define EXATTN_FWD_WAVES 2
 #endif
 
 namespace exattn {
@@ -59,6 +62,10 @@ struct FwdLds {
   static constexpr int bytes = 4 * tile * 2;        // K, V x double buffer
 };
 
+// Prefetch depth in tiles: two where the second register set fits.
+template <int D>
+constexpr int fwd_prefetch() { return D <= 80 ? 2 : 1; }
+
 template <int D, int QW, bool OUT_F32>
 __global__ __launch_bounds__(fwdk::NT)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? EXATTN_FWD_WAVES : 2)))
@@ -70,6 +77,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = 4 * QW;            // query rows per workgroup
   constexpr int CH = BN * (D / 8);      // 16-byte pieces per tile
   constexpr int PT = (CH + NT - 1) / NT;
+  constexpr int PF = fwd_prefetch<D>();
   __shared__ __attribute__((aligned(16))) bf16 lds[4 * L::tile];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -108,19 +116,25 @@ void fwd_bf16_kernel(FwdArgs a) {
                                  : zero8;
   }
 
-  // tile loader: piece e -> row e / (D/8), 16-byte column piece e % (D/8)
-  bf16x8 pk[PT], pv[PT];
-  auto load_tile = [&](int j0) {
+  // Tile loader with two register sets.  With PF = 2, tile t goes global ->
+  // set t % 2 (issued two tiles ahead) -> LDS buffer t % 2 (stored one tile
+  // ahead), so each load has two tiles of work to land; with PF = 1 the load
+  // is issued one tile ahead.  Piece e -> row e / (D/8), 16-byte column piece
+  // e % (D/8).
+  bf16x8 pk[2][PT], pv[2][PT];
+  auto load_tile = [&](auto set_tag, int j0) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
       const int r = e / (D / 8), cc = e % (D / 8);
       const bool ok = e < CH && j0 + r < n_kv;
-      pk[u] = ok ? load_bf16x8(kp + (int64_t)(j0 + r) * a.ks.sn + 8 * cc) : zero8;
-      pv[u] = ok ? load_bf16x8(vp + (int64_t)(j0 + r) * a.vs.sn + 8 * cc) : zero8;
+      pk[S][u] = ok ? load_bf16x8(kp + (int64_t)(j0 + r) * a.ks.sn + 8 * cc) : zero8;
+      pv[S][u] = ok ? load_bf16x8(vp + (int64_t)(j0 + r) * a.vs.sn + 8 * cc) : zero8;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto set_tag, int buf) {
+    constexpr int S = decltype(set_tag)::value;
     bf16* Kt = lds + buf * 2 * L::tile;
     bf16* Vt = Kt + L::tile;
 #pragma unroll
@@ -128,11 +142,13 @@ void fwd_bf16_kernel(FwdArgs a) {
       const int e = tid + u * NT;
       if (e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
-        *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[u];
-        *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[u];
+        *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[S][u];
+        *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[S][u];
       }
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   f32x16 oacc[NDB][NQB];
 #pragma unroll
@@ -149,15 +165,20 @@ void fwd_bf16_kernel(FwdArgs a) {
   const float lazy = kLazy / sl2;  // threshold in raw score units
 
   if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_tile(S0{}, 0);
+    store_tile(S0{}, 0);
   }
+  if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One key/value tile.  MASKED is set only for the ragged last tile, so the
+  // full tiles carry no masking code at all.
+  // With PF = 1 a single register set is used (load and store sets 0) and
+  // the LDS buffer alternates at run time.
+  auto tile = [&](auto masked_tag, auto load_set, auto store_set, int it, int buf) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = it * BN;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(j0 + BN);
+    if (it + PF < ntiles) load_tile(load_set, j0 + PF * BN);
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
@@ -174,7 +195,7 @@ void fwd_bf16_kernel(FwdArgs a) {
           for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
         }
       }
-      if (j0 + BN > n_kv) {  // ragged last tile: keys past the end weigh nothing
+      if constexpr (MASKED) {  // keys past the end weigh nothing
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -241,8 +262,31 @@ void fwd_bf16_kernel(FwdArgs a) {
         }
       }
     }
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    if (it + 1 < ntiles) store_tile(store_set, buf ^ 1);
     __syncthreads();
+  };
+  const int nfull = n_kv / BN;
+  int it = 0;
+  if constexpr (PF == 2) {
+    // SET = it % 2: the LDS buffer read now and the register set receiving
+    // tile it + 2; the other set holds tile it + 1
+    for (; it + 1 < nfull; it += 2) {
+      tile(std::false_type{}, S0{}, S1{}, it, 0);
+      tile(std::false_type{}, S1{}, S0{}, it + 1, 1);
+    }
+    if (it < nfull) {
+      tile(std::false_type{}, S0{}, S1{}, it, 0);
+      ++it;
+    }
+    if (it < ntiles) {  // the ragged last tile, in whichever set it falls
+      if (it & 1)
+        tile(std::true_type{}, S1{}, S0{}, it, 1);
+      else
+        tile(std::true_type{}, S0{}, S1{}, it, 0);
+    }
+  } else {
+    for (; it < nfull; ++it) tile(std::false_type{}, S0{}, S0{}, it, it & 1);
+    if (it < ntiles) tile(std::true_type{}, S0{}, S0{}, it, it & 1);
   }
 
   if (!wave_active) return;
@@ -277,6 +321,233 @@ void fwd_bf16_kernel(FwdArgs a) {
       const int64_t li = (int64_t)c * a.lse_chunk_stride + ((int64_t)b * a.H + h) * a.Nq + qrow;
       a.lse[li] = l > 0.f ? (mref[qb] * sl2 + log2f(l)) * kLn2 : -INFINITY;
     }
+  }
+}
+
+// --------------------------------------------------------------------------
+// bf16 forward, ping-pong variant for long query sequences (d = 64, 80).
+//
+// Workgroup: 8 waves in two groups of four; wave w and wave w + 4 share a
+// SIMD (group = w / 4 by default).  Each wave owns 32 query rows (256 per
+// workgroup).  Per tile, a wave runs a matrix phase M(j) -- S_j = K_j Q^T
+// and O^T += V_{j-1}^T P_{j-1}^T -- and a vector phase V(j) -- maximum, lazy
+// rescale, P_j = exp2(S_j - m), row sums.  Group 1 runs one phase behind
+// group 0, and a barrier separates phases, so on every SIMD one wave's
+// matrix instructions overlap the other wave's vector instructions.
+//
+// LDS holds two K slots and two V slots.  Around phase step 2t all waves
+// store K_{t+1} (slot (t+1) % 2) and V_t (slot t % 2) from registers loaded
+// one tile earlier: K_j is read in steps 2j, 2j+1 and V_j in 2j+2, 2j+3, so a
+// slot is rewritten only after both groups are done with it.
+// --------------------------------------------------------------------------
+#ifndef EXATTN_PP_GROUP_BY_HALF
+#define EXATTN_PP_GROUP_BY_HALF 1
+#endif
+
+namespace ppk {
+constexpr int BN = 64;
+constexpr int NT = 512;
+constexpr int QW = 32;
+constexpr int BM = 8 * QW;
+}  // namespace ppk
+
+template <int D>
+struct PpLds {
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int KS = DP + 8;
+  static constexpr int tile = ppk::BN * KS;
+  static constexpr int bytes = 4 * tile * 2;  // K x 2 slots, V x 2 slots
+};
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(ppk::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_pp_kernel(FwdArgs a) {
+  using namespace ppk;
+  using L = PpLds<D>;
+  constexpr int DP = L::DP, NDB = DP / 32, KC = D / 16, KS = L::KS;
+  constexpr int CH = BN * (D / 8);
+  constexpr int PT = (CH + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) bf16 lds[4 * L::tile];
+  bf16* const Kslot = lds;                  // [2][tile]
+  bf16* const Vslot = lds + 2 * L::tile;    // [2][tile]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ln = lane & 31, g = lane >> 5;
+  const int grp = EXATTN_PP_GROUP_BY_HALF ? (w >> 2) : (w & 1);
+
+  const int nqb = (a.Nq + BM - 1) / BM;
+  int idx = xcd_remap(blockIdx.x, gridDim.x);
+  const int qblk = idx % nqb;
+  idx /= nqb;
+  const int h = idx % a.H;
+  const int b = idx / a.H;
+  const int n_kv = a.Nkv;
+  const int ntiles = (n_kv + BN - 1) / BN;
+
+  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh;
+
+  const int q0 = qblk * BM + w * QW;
+  const bool wave_active = q0 < a.Nq;
+  const int qrow = q0 + ln;
+  const bf16x8 zero8 = {};
+
+  bf16x8 qreg[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    qreg[kc] = qrow < a.Nq ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g) : zero8;
+
+  // prefetch registers for one (K_{t+1}, V_t) pair
+  bf16x8 pk[PT], pv[PT];
+  auto load_rows = [&](const bf16* base, int64_t sn, int j0, bf16x8* dst) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      const int r = e / (D / 8), cc = e % (D / 8);
+      dst[u] = (e < CH && j0 + r < n_kv) ? load_bf16x8(base + (int64_t)(j0 + r) * sn + 8 * cc)
+                                         : zero8;
+    }
+  };
+  auto store_rows = [&](bf16* slot, const bf16x8* src) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      if (e < CH) {
+        const int r = e / (D / 8), cc = e % (D / 8);
+        *reinterpret_cast<bf16x8*>(&slot[r * KS + 8 * cc]) = src[u];
+      }
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  f32x16 s[2];
+  bf16x8 pb[4];
+  float mref = -INFINITY, lsum = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  const float lazy = fwdk::kLazy / sl2;
+
+  // prologue: K_0 into slot 0; the pair (K_1, V_0) into registers
+  load_rows(kp, a.ks.sn, 0, pk);
+  store_rows(Kslot, pk);
+  load_rows(kp, a.ks.sn, BN, pk);
+  load_rows(vp, a.vs.sn, 0, pv);
+  __syncthreads();
+
+  // matrix phase M(j): S_j (if j < ntiles) and PV of tile j - 1 (if j >= 1)
+  auto mphase = [&](int j) {
+    if (j < ntiles) {
+      const bf16* Kt = Kslot + (j & 1) * L::tile;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        s[cb] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+          s[cb] = mfma32(ka, qreg[kc], s[cb]);
+        }
+      }
+    }
+    if (j >= 1) {
+      const bf16* Vt = Vslot + ((j - 1) & 1) * L::tile;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+          oacc[db] = mfma32(va, pb[t], oacc[db]);
+        }
+    }
+  };
+  // vector phase V(j): P_j from S_j
+  auto vphase = [&](int j) {
+    const int j0 = j * BN;
+    if (j0 + BN > n_kv) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3) >= n_kv) s[cb][e] = -INFINITY;
+    }
+    float m = s[0][0];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, s[cb][e]);
+    const float mx = max_halves(m);
+    if (__builtin_amdgcn_ballot_w64(mx > mref + lazy)) {
+      const float mnew = fmaxf(mref, mx);
+      const float alpha = fast_exp2((mref - mnew) * sl2);
+      mref = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    const float moff = mref * sl2;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(fmaf(s[cb][e], sl2, -moff));
+        s[cb][e] = p;
+        part[e & 3] += p;
+      }
+    lsum += (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
+  };
+
+  // phase p of a group: even -> M(p / 2), odd -> V((p - 1) / 2); 2 ntiles + 1
+  // phases per group, group 1 one step behind group 0
+  const int nphase = 2 * ntiles + 1;
+  for (int step = 0; step < nphase + 1; ++step) {
+    if ((step & 1) == 0) {
+      // pair t = step / 2: store (K_{t+1}, V_t), then load the next pair
+      const int t = step >> 1;
+      if (t + 1 < ntiles) store_rows(Kslot + ((t + 1) & 1) * L::tile, pk);
+      if (t < ntiles) store_rows(Vslot + (t & 1) * L::tile, pv);
+      if (t + 2 < ntiles) load_rows(kp, a.ks.sn, (t + 2) * BN, pk);
+      if (t + 1 < ntiles) load_rows(vp, a.vs.sn, (t + 1) * BN, pv);
+    }
+    const int p = step - grp;
+    if (wave_active && p >= 0 && p < nphase) {
+      if ((p & 1) == 0)
+        mphase(p >> 1);
+      else
+        vphase(p >> 1);
+    }
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  const float l = sum_halves(lsum);
+  if (qrow >= a.Nq) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t orow = b * a.os.sb + h * a.os.sh + (int64_t)qrow * a.os.sn;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * db + 8 * i + 4 * g;
+      if (d0 < D) {
+        const f32x16& o = oacc[db];
+        if constexpr (OUT_F32) {
+          f32x4 v4 = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv, o[4 * i + 3] * inv};
+          *reinterpret_cast<f32x4*>((float*)a.o + orow + d0) = v4;
+        } else {
+          bf16x4 v4 = {(bf16)(o[4 * i] * inv), (bf16)(o[4 * i + 1] * inv),
+                       (bf16)(o[4 * i + 2] * inv), (bf16)(o[4 * i + 3] * inv)};
+          *reinterpret_cast<bf16x4*>((bf16*)a.o + orow + d0) = v4;
+        }
+      }
+    }
+  }
+  if (g == 0) {
+    const int64_t li = ((int64_t)b * a.H + h) * a.Nq + qrow;
+    a.lse[li] = l > 0.f ? (mref * sl2 + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -362,8 +633,28 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   a.lse[li] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+#ifndef EXATTN_FWD_PP
+#define EXATTN_FWD_PP 0
+#endif
+
+template <int D>
+static hipError_t fwd_pp_d(const FwdArgs& a, hipStream_t s) {
+  const int nqb = (a.Nq + ppk::BM - 1) / ppk::BM;
+  const long long grid = (long long)nqb * a.H * a.B;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.out_f32)
+    hipLaunchKernelGGL((fwd_pp_kernel<D, true>), dim3((unsigned)grid), dim3(ppk::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_pp_kernel<D, false>), dim3((unsigned)grid), dim3(ppk::NT), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int QW>
 static hipError_t fwd_bf16_d(const FwdArgs& a, hipStream_t s) {
+  if constexpr (D <= 80) {
+    // long query sequences, one key/value range: the ping-pong kernel
+    if (EXATTN_FWD_PP && a.n_chunks == 1 && a.Nq >= ppk::BM) return fwd_pp_d<D>(a, s);
+  }
   const int nqb = (a.Nq + 4 * QW - 1) / (4 * QW);
   const long long grid = (long long)nqb * a.H * a.B * a.n_chunks;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
