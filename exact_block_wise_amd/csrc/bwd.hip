@@ -285,6 +285,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
           da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
         }
         f32x16 s[NCB], dp[NCB];
+        prio_mfma();
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           s[cb] = f32x16{};
@@ -295,6 +296,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
             dp[cb] = mfma32(da[kc], vreg[cb][kc], dp[cb]);
           }
         }
+        prio_valu();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int qi = 32 * nb + 8 * i + 4 * g;
@@ -311,6 +313,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
         }
         // dV += P^T dO, dK += dS^T Q over two 16-query chunks t = 2 nb + hh:
         // slot group g holds queries 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3)
+        prio_mfma();
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int t = 2 * nb + hh;
@@ -336,6 +339,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
             }
           }
         }
+        prio_valu();
       }
     }
     if (it + 1 < nqt) store_tile(buf ^ 1);
@@ -483,6 +487,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
       f32x16 st[2][NQB], dpt[2][NQB];
+      prio_mfma();
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
@@ -501,6 +506,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
           }
         }
       }
+      prio_valu();
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -512,6 +518,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
           }
       // dQ += dS K over four 16-key chunks (slot group g: keys 16t + 4g +
       // (0..3) and 16t + 8 + 4g + (0..3) = accumulator entries 8hh..8hh+7)
+      prio_mfma();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         bf16x8 sa[NQB];
@@ -524,6 +531,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
           for (int qb = 0; qb < NQB; ++qb) dq[qb][db] = mfma32(sa[qb], kb8, dq[qb][db]);
         }
       }
+      prio_valu();
     }
     if (it + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();

@@ -49,6 +49,19 @@ __device__ __forceinline__ void agpr_results_ready() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// Wave priority around matrix-instruction blocks: a wave about to issue
+// products is favoured, so co-resident waves in their vector phase fill the
+// gaps instead of all waves reaching the matrix unit at once.
+#ifndef EXATTN_SETPRIO
+#define EXATTN_SETPRIO 0
+#endif
+__device__ __forceinline__ void prio_mfma() {
+  if constexpr (EXATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void prio_valu() {
+  if constexpr (EXATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }

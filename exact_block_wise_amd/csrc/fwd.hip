@@ -62,6 +62,11 @@ struct FwdLds {
   static constexpr int bytes = 4 * tile * 2;        // K, V x double buffer
 };
 
+// Issue each tile's LDS operand reads in bulk ahead of their products.
+#ifndef EXATTN_FWD_STAGED
+#define EXATTN_FWD_STAGED 0
+#endif
+
 // Prefetch depth in tiles: two where the second register set fits.
 template <int D>
 constexpr int fwd_prefetch() { return D <= 80 ? 2 : 1; }
@@ -184,16 +189,47 @@ void fwd_bf16_kernel(FwdArgs a) {
       const bf16* Vt = Kt + L::tile;
       // S^T = K Q^T for two 32-key blocks x NQB query blocks
       f32x16 s[2][NQB];
+      bf16x8 va[4][NDB];
+      if constexpr (EXATTN_FWD_STAGED) {
+        // all K operand reads first, then the products; the V operands are
+        // read next so that they land while the softmax runs
+        bf16x8 ka[2][KC];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+          for (int kc = 0; kc < KC; ++kc)
+            ka[cb][kc] = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+        for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
+          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka[cb][kc], qreg[qb][kc], s[cb][qb]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            va[t][db] = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        prio_mfma();
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
+          }
+        }
+        prio_valu();
       }
       if constexpr (MASKED) {  // keys past the end weigh nothing
 #pragma unroll
@@ -252,15 +288,18 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) pb[t][qb] = acc_half_to_bf16(s[t >> 1][qb], t & 1);
       }
+      prio_mfma();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+          if constexpr (!EXATTN_FWD_STAGED)
+            va[t][db] = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = mfma32(va, pb[t][qb], oacc[db][qb]);
+          for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = mfma32(va[t][db], pb[t][qb], oacc[db][qb]);
         }
       }
+      prio_valu();
     }
     if (it + 1 < ntiles) store_tile(store_set, buf ^ 1);
     __syncthreads();
@@ -321,6 +360,293 @@ void fwd_bf16_kernel(FwdArgs a) {
       const int64_t li = (int64_t)c * a.lse_chunk_stride + ((int64_t)b * a.H + h) * a.Nq + qrow;
       a.lse[li] = l > 0.f ? (mref[qb] * sl2 + log2f(l)) * kLn2 : -INFINITY;
     }
+  }
+}
+
+// --------------------------------------------------------------------------
+// bf16 forward, software-pipelined (d = 64, 80).
+//
+// Same workgroup shape as fwd_bf16_kernel (4 waves x 32 query rows), but
+// each wave overlaps the matrix and vector work of consecutive tiles:
+//   step a:  S_{j+1} = K_{j+1} Q^T         ||  P_j = exp2(S_j - m), sums, cvt
+//   step b:  O^T += V_j^T P_j^T            ||  max of S_{j+1}, rescale test
+//   step c:  (rare) rescale O and l after PV_j, raise the reference for j+1
+// Steps a and b are single branch-free regions in which scheduling hints
+// alternate matrix instructions with vector instructions.  K is needed one
+// tile ahead of V, so LDS holds three K slots and two V slots; the pair
+// (K_{j+2}, V_{j+1}) is loaded during iteration j and stored at its end.
+// --------------------------------------------------------------------------
+#ifndef EXATTN_FWD_SP
+#define EXATTN_FWD_SP 0
+#endif
+#ifndef EXATTN_SP_HINTS
+#define EXATTN_SP_HINTS 1
+#endif
+
+namespace spk {
+constexpr int BN = 64;
+constexpr int NT = 256;
+constexpr int QW = 32;
+constexpr int BM = 4 * QW;
+}  // namespace spk
+
+template <int D>
+struct SpLds {
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int KS = DP + 8;
+  static constexpr int tile = spk::BN * KS;
+  static constexpr int bytes = 5 * tile * 2;  // K x 3 slots, V x 2 slots
+};
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(spk::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_sp_kernel(FwdArgs a) {
+  using namespace spk;
+  using L = SpLds<D>;
+  constexpr int DP = L::DP, NDB = DP / 32, KC = D / 16, KS = L::KS;
+  constexpr int CH = BN * (D / 8);
+  constexpr int PT = (CH + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) bf16 lds[5 * L::tile];
+  bf16* const Kslot = lds;                  // [3][tile]
+  bf16* const Vslot = lds + 3 * L::tile;    // [2][tile]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ln = lane & 31, g = lane >> 5;
+
+  const int nqb = (a.Nq + BM - 1) / BM;
+  int idx = xcd_remap(blockIdx.x, gridDim.x);
+  const int qblk = idx % nqb;
+  idx /= nqb;
+  const int h = idx % a.H;
+  idx /= a.H;
+  const int b = idx % a.B;
+  const int c = idx / a.B;
+
+  const int kv_lo = c * a.chunk_len;
+  const int n_kv = max(0, min(a.Nkv, kv_lo + a.chunk_len) - kv_lo);
+  const int ntiles = (n_kv + BN - 1) / BN;
+  const bool ragged = (n_kv % BN) != 0;
+
+  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh + (int64_t)kv_lo * a.ks.sn;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh + (int64_t)kv_lo * a.vs.sn;
+
+  const int q0 = qblk * BM + w * QW;
+  const bool wave_active = q0 < a.Nq;
+  const int qrow = q0 + ln;
+  const bf16x8 zero8 = {};
+
+  bf16x8 qreg[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    qreg[kc] = qrow < a.Nq ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g) : zero8;
+
+  bf16x8 pk[PT], pv[PT];
+  auto load_rows = [&](const bf16* base, int64_t sn, int j0, bf16x8* dst) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      const int r = e / (D / 8), cc = e % (D / 8);
+      dst[u] = (e < CH && j0 + r < n_kv) ? load_bf16x8(base + (int64_t)(j0 + r) * sn + 8 * cc)
+                                         : zero8;
+    }
+  };
+  auto store_rows = [&](bf16* slot, const bf16x8* src) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      if (e < CH) {
+        const int r = e / (D / 8), cc = e % (D / 8);
+        *reinterpret_cast<bf16x8*>(&slot[r * KS + 8 * cc]) = src[u];
+      }
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  f32x16 scur[2], snxt[2];
+  float mref = -INFINITY, lsum = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  const float lazy = fwdk::kLazy / sl2;
+
+  auto scores = [&](int j, f32x16* sdst) {
+    const bf16* Kt = Kslot + (j % 3) * L::tile;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      sdst[cb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+        sdst[cb] = mfma32(ka, qreg[kc], sdst[cb]);
+      }
+    }
+  };
+  auto mask = [&](int j, f32x16* sv) {
+    const int j0 = j * BN;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3) >= n_kv) sv[cb][e] = -INFINITY;
+  };
+  auto rowmax = [&](const f32x16* sv) {
+    float m = sv[0][0];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, sv[cb][e]);
+    return max_halves(m);
+  };
+  // (rare) raise the reference to mx; O and l hold tiles up to the current one
+  auto raise_ref = [&](float mx) {
+    const float mnew = fmaxf(mref, mx);
+    const float alpha = fast_exp2((mref - mnew) * sl2);
+    mref = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+  };
+
+  // prologue: K_0, K_1, V_0 in LDS; S_0 and its reference maximum
+  if (ntiles > 0) {
+    load_rows(kp, a.ks.sn, 0, pk);
+    store_rows(Kslot, pk);
+    load_rows(vp, a.vs.sn, 0, pv);
+    store_rows(Vslot, pv);
+  }
+  if (ntiles > 1) {
+    load_rows(kp, a.ks.sn, BN, pk);
+    store_rows(Kslot + L::tile, pk);
+  }
+  __syncthreads();
+  if (wave_active && ntiles > 0) {
+    scores(0, scur);
+    if (ntiles == 1 && ragged) mask(0, scur);
+    raise_ref(rowmax(scur));
+  }
+
+  // iteration j; NEXT: tile j + 1 exists, MASKN: it is the ragged last tile
+  auto iteration = [&](auto next_tag, auto maskn_tag, int j) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr bool MASKN = decltype(maskn_tag)::value;
+    if (j + 2 < ntiles) load_rows(kp, a.ks.sn, (j + 2) * BN, pk);
+    if (j + 1 < ntiles) load_rows(vp, a.vs.sn, (j + 1) * BN, pv);
+    if (wave_active) {
+      // step a: S_{j+1} || softmax of S_j.  The K operands are read first,
+      // so that the products need no LDS wait once they start.
+      bf16x8 ka[2][KC];
+      if constexpr (NEXT) {
+        const bf16* Kt = Kslot + ((j + 1) % 3) * L::tile;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            ka[cb][kc] = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          snxt[cb] = f32x16{};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) snxt[cb] = mfma32(ka[cb][kc], qreg[kc], snxt[cb]);
+        }
+      }
+      const float moff = mref * sl2;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(fmaf(scur[cb][e], sl2, -moff));
+          scur[cb][e] = p;
+          part[e & 3] += p;
+        }
+      lsum += (part[0] + part[1]) + (part[2] + part[3]);
+      bf16x8 pb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pb[t] = acc_half_to_bf16(scur[t >> 1], t & 1);
+      if constexpr (EXATTN_SP_HINTS && NEXT) {
+#pragma unroll
+        for (int k = 0; k < 2 * KC; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // a product
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // vector work
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // step b: PV_j || maximum of S_{j+1}
+      const bf16* Vt = Vslot + (j & 1) * L::tile;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+          oacc[db] = mfma32(va, pb[t], oacc[db]);
+        }
+      float mx = 0.f;
+      if constexpr (NEXT) {
+        if constexpr (MASKN) mask(j + 1, snxt);
+        mx = rowmax(snxt);
+      }
+      if constexpr (EXATTN_SP_HINTS) {
+#pragma unroll
+        for (int k = 0; k < 4 * NDB; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // step c: rare rescale, after PV_j is in O
+      if constexpr (NEXT) {
+        if (__builtin_amdgcn_ballot_w64(mx > mref + lazy)) raise_ref(mx);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) scur[cb] = snxt[cb];
+      }
+    }
+    if (j + 2 < ntiles) store_rows(Kslot + ((j + 2) % 3) * L::tile, pk);
+    if (j + 1 < ntiles) store_rows(Vslot + ((j + 1) & 1) * L::tile, pv);
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 2 < ntiles; ++j) iteration(std::true_type{}, std::false_type{}, j);
+  if (j + 1 < ntiles) {
+    if (ragged)
+      iteration(std::true_type{}, std::true_type{}, j);
+    else
+      iteration(std::true_type{}, std::false_type{}, j);
+    ++j;
+  }
+  if (j < ntiles) iteration(std::false_type{}, std::false_type{}, j);
+
+  if (!wave_active) return;
+  const float l = sum_halves(lsum);
+  if (qrow >= a.Nq) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t orow = (int64_t)c * a.o_chunk_stride + b * a.os.sb + h * a.os.sh +
+                       (int64_t)qrow * a.os.sn;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * db + 8 * i + 4 * g;
+      if (d0 < D) {
+        const f32x16& o = oacc[db];
+        if constexpr (OUT_F32) {
+          f32x4 v4 = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv, o[4 * i + 3] * inv};
+          *reinterpret_cast<f32x4*>((float*)a.o + orow + d0) = v4;
+        } else {
+          bf16x4 v4 = {(bf16)(o[4 * i] * inv), (bf16)(o[4 * i + 1] * inv),
+                       (bf16)(o[4 * i + 2] * inv), (bf16)(o[4 * i + 3] * inv)};
+          *reinterpret_cast<bf16x4*>((bf16*)a.o + orow + d0) = v4;
+        }
+      }
+    }
+  }
+  if (g == 0) {
+    const int64_t li = (int64_t)c * a.lse_chunk_stride + ((int64_t)b * a.H + h) * a.Nq + qrow;
+    a.lse[li] = l > 0.f ? (mref * sl2 + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -649,9 +975,22 @@ static hipError_t fwd_pp_d(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t fwd_sp_d(const FwdArgs& a, hipStream_t s) {
+  const int nqb = (a.Nq + spk::BM - 1) / spk::BM;
+  const long long grid = (long long)nqb * a.H * a.B * a.n_chunks;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.out_f32)
+    hipLaunchKernelGGL((fwd_sp_kernel<D, true>), dim3((unsigned)grid), dim3(spk::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_sp_kernel<D, false>), dim3((unsigned)grid), dim3(spk::NT), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int QW>
 static hipError_t fwd_bf16_d(const FwdArgs& a, hipStream_t s) {
   if constexpr (D <= 80) {
+    if (EXATTN_FWD_SP) return fwd_sp_d<D>(a, s);
     // long query sequences, one key/value range: the ping-pong kernel
     if (EXATTN_FWD_PP && a.n_chunks == 1 && a.Nq >= ppk::BM) return fwd_pp_d<D>(a, s);
   }
