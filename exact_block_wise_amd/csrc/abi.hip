@@ -12,6 +12,7 @@ using namespace exattn;
 namespace {
 
 constexpr size_t kWsAlign = 256;
+constexpr int64_t kMaxRowStrideBytes = int64_t(1) << 24;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -36,6 +37,8 @@ attn_status check_tensor(const attn_tensor& t) {
   const int64_t vec = 16 / elem_bytes(t.dtype);
   if (reinterpret_cast<uintptr_t>(t.ptr) % 16 != 0) return ATTN_E_UNSUPPORTED;
   if (t.sb % vec || t.sh % vec || t.sn % vec) return ATTN_E_UNSUPPORTED;
+  // a tile of up to 128 rows must stay within 32-bit buffer offsets
+  if (t.sn * elem_bytes(t.dtype) > kMaxRowStrideBytes) return ATTN_E_UNSUPPORTED;
   return ATTN_OK;
 }
 

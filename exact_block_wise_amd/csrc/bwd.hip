@@ -9,6 +9,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 #include <math.h>
 
 
@@ -93,7 +95,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   bf16* const lds = reinterpret_cast<bf16*>(smem);
   float* const stats = reinterpret_cast<float*>(lds + L::n_bf16);  // [2][LSE2 | D][BM]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, g = lane >> 5;
 
   const int nkb = (a.Nkv + BN - 1) / BN;
@@ -112,38 +115,50 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 
   const int kw = kb * BN + KW * w;             // first key row of this wave
   const bool wave_active = kw < a.Nkv;
-  const bf16x8 zero8 = {};
 
   // this wave's K and V rows as B operands (lane: key kw + 32cb + ln,
-  // d = 16kc + 8g .. +7)
+  // d = 16kc + 8g .. +7; rows past Nkv read as zeros)
   bf16x8 kreg[NCB][KC], vreg[NCB][KC];
+  {
+    const auto rk = rows_rsrc(kp + (int64_t)kw * a.ks.sn, a.Nkv - kw, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)kw * a.vs.sn, a.Nkv - kw, 2 * a.vs.sn, 2 * D);
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int krow = kw + 32 * cb + ln;
-    const bool ok = krow < a.Nkv;
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      kreg[cb][kc] = ok ? load_bf16x8(kp + (int64_t)krow * a.ks.sn + 16 * kc + 8 * g) : zero8;
-      vreg[cb][kc] = ok ? load_bf16x8(vp + (int64_t)krow * a.vs.sn + 16 * kc + 8 * g) : zero8;
-    }
+      for (int kc = 0; kc < KC; ++kc) {
+        const int col = 2 * (16 * kc + 8 * g);
+        kreg[cb][kc] = buffer_load_bf16x8(rk, (uint32_t)((32 * cb + ln) * 2 * a.ks.sn + col));
+        vreg[cb][kc] = buffer_load_bf16x8(rv, (uint32_t)((32 * cb + ln) * 2 * a.vs.sn + col));
+      }
   }
 
+  // Query tile loader: unconditional buffer loads (rows past Nq come back as
+  // zeros; their LSE is then set to +inf so that P = 0), so no branch sits
+  // between a load and the wait before its LDS store.
+  uint32_t qoff[PT], doff[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = tid + u * NT;
+    const int r = e / (D / 8), cc = e % (D / 8);
+    qoff[u] = (uint32_t)(r * 2 * a.qs.sn + 16 * cc);
+    doff[u] = (uint32_t)(r * 2 * a.dos.sn + 16 * cc);
+  }
   bf16x8 pq[PT], pd[PT];
   float pst = 0.f;
   auto load_tile = [&](int q0) {
+    const int rows = a.Nq - q0;
+    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
+    const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int e = tid + u * NT;
-      const int r = e / (D / 8), cc = e % (D / 8);
-      const bool ok = e < CH && q0 + r < a.Nq;
-      pq[u] = ok ? load_bf16x8(qp + (int64_t)(q0 + r) * a.qs.sn + 8 * cc) : zero8;
-      pd[u] = ok ? load_bf16x8(dop + (int64_t)(q0 + r) * a.dos.sn + 8 * cc) : zero8;
+      pq[u] = buffer_load_bf16x8(rq, qoff[u]);
+      pd[u] = buffer_load_bf16x8(rd, doff[u]);
     }
-    if (tid < 2 * BM) {
-      const int r = tid & (BM - 1);
-      const bool ok = q0 + r < a.Nq;
-      pst = tid < BM ? (ok ? lsep[q0 + r] * kLog2e : INFINITY) : (ok ? dsp[q0 + r] : 0.f);
-    }
+    // threads 0 .. BM-1: LSE (log2 units) of query q0 + tid; BM .. 2BM-1: D
+    const int r = tid & (BM - 1);
+    const float l = buffer_load_f32(rows_rsrc(lsep + q0, rows, 4, 4), 4 * r);
+    const float dd = buffer_load_f32(rows_rsrc(dsp + q0, rows, 4, 4), 4 * r);
+    pst = tid < BM ? (r < rows ? l * kLog2e : INFINITY) : dd;
   };
   auto store_tile = [&](int buf) {
     bf16* Qs = lds + buf * 2 * L::tile;
@@ -151,7 +166,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
-      if (e < CH) {
+      if (CH % NT == 0 || e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
         *reinterpret_cast<bf16x8*>(&Qs[r * RS + 8 * cc]) = pq[u];
         *reinterpret_cast<bf16x8*>(&dOs[r * RS + 8 * cc]) = pd[u];
@@ -258,13 +273,12 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     dvdk(1, s1, dp1);
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int it = 0; it < nqt; ++it) {
+  // One query tile; NEXT: tile it + 1 exists (its loads are issued before
+  // and stored after this tile's work, without a run-time test).
+  auto tile = [&](auto next_tag, int it) {
+    constexpr bool NEXT = decltype(next_tag)::value;
     const int buf = it & 1;
-    if (it + 1 < nqt) load_tile((it + 1) * BM);
+    if (NEXT) load_tile((it + 1) * BM);
     if (wave_active) {
       const bf16* Qs = lds + buf * 2 * L::tile;
       const bf16* dOs = Qs + L::tile;
@@ -342,9 +356,15 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
         prio_valu();
       }
     }
-    if (it + 1 < nqt) store_tile(buf ^ 1);
+    if (NEXT) store_tile(buf ^ 1);
     __syncthreads();
-  }
+  };
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  int it = 0;
+  for (; it + 1 < nqt; ++it) tile(std::true_type{}, it);
+  tile(std::false_type{}, it);
 
   if (!wave_active) return;
   if constexpr (kPinAcc) agpr_results_ready();
@@ -406,7 +426,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16* const lds = reinterpret_cast<bf16*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, g = lane >> 5;
 
   const int nqb = (a.Nq + BM - 1) / BM;
@@ -425,34 +446,51 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
 
   const int q0 = qblk * BM + w * QW;
   const bool wave_active = q0 < a.Nq;
-  const bf16x8 zero8 = {};
 
+  // this wave's Q and dO rows as B operands, with their LSE (log2 units) and
+  // D; rows past Nq read as zeros with LSE = +inf
   bf16x8 qreg[NQB][KC], doreg[NQB][KC];
   float lse2[NQB], dsum[NQB];
+  {
+    const int rows = a.Nq - q0;
+    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
+    const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
+    const auto rl = rows_rsrc(lsep + q0, rows, 4, 4);
+    const auto rs = rows_rsrc(dsp + q0, rows, 4, 4);
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qrow = q0 + 32 * qb + ln;
-    const bool ok = qrow < a.Nq;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int r = 32 * qb + ln;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      qreg[qb][kc] = ok ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g) : zero8;
-      doreg[qb][kc] = ok ? load_bf16x8(dop + (int64_t)qrow * a.dos.sn + 16 * kc + 8 * g) : zero8;
+      for (int kc = 0; kc < KC; ++kc) {
+        const int col = 2 * (16 * kc + 8 * g);
+        qreg[qb][kc] = buffer_load_bf16x8(rq, (uint32_t)(r * 2 * a.qs.sn + col));
+        doreg[qb][kc] = buffer_load_bf16x8(rd, (uint32_t)(r * 2 * a.dos.sn + col));
+      }
+      const float l = buffer_load_f32(rl, 4 * r);
+      lse2[qb] = r < rows ? l * kLog2e : INFINITY;
+      dsum[qb] = buffer_load_f32(rs, 4 * r);
     }
-    lse2[qb] = ok ? lsep[qrow] * kLog2e : INFINITY;
-    dsum[qb] = ok ? dsp[qrow] : 0.f;
   }
 
   const int n_kv = a.Nkv;
   const int ntiles = (n_kv + BN - 1) / BN;
+  // key/value tile loader: unconditional buffer loads, rows past Nkv zero
+  uint32_t koff[PT], voff[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = tid + u * NT;
+    const int r = e / (D / 8), cc = e % (D / 8);
+    koff[u] = (uint32_t)(r * 2 * a.ks.sn + 16 * cc);
+    voff[u] = (uint32_t)(r * 2 * a.vs.sn + 16 * cc);
+  }
   bf16x8 pk[PT], pv[PT];
   auto load_tile = [&](int j0) {
+    const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int e = tid + u * NT;
-      const int r = e / (D / 8), cc = e % (D / 8);
-      const bool ok = e < CH && j0 + r < n_kv;
-      pk[u] = ok ? load_bf16x8(kp + (int64_t)(j0 + r) * a.ks.sn + 8 * cc) : zero8;
-      pv[u] = ok ? load_bf16x8(vp + (int64_t)(j0 + r) * a.vs.sn + 8 * cc) : zero8;
+      pk[u] = buffer_load_bf16x8(rk, koff[u]);
+      pv[u] = buffer_load_bf16x8(rv, voff[u]);
     }
   };
   auto store_tile = [&](int buf) {
@@ -461,7 +499,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
-      if (e < CH) {
+      if (CH % NT == 0 || e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
         *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[u];
         *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[u];
@@ -476,13 +514,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     for (int db = 0; db < NDB; ++db) dq[qb][db] = f32x16{};
   const float sl2 = a.scale * kLog2e;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
+  // One key/value tile; NEXT: tile it + 1 exists (loaded before and stored
+  // after this tile's work, without a run-time test).
+  auto tile = [&](auto next_tag, int it) {
+    constexpr bool NEXT = decltype(next_tag)::value;
     const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile((it + 1) * BN);
+    if (NEXT) load_tile((it + 1) * BN);
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
@@ -533,9 +570,15 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       }
       prio_valu();
     }
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+    if (NEXT) store_tile(buf ^ 1);
     __syncthreads();
-  }
+  };
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  int it = 0;
+  for (; it + 1 < ntiles; ++it) tile(std::true_type{}, it);
+  tile(std::false_type{}, it);
 
   if (!wave_active) return;
   // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block

@@ -141,6 +141,28 @@ __device__ __forceinline__ bf16x8 acc_half_to_bf16(const f32x16& s, int h) {
               s[8 * h + 4], s[8 * h + 5], s[8 * h + 6], s[8 * h + 7]);
 }
 
+// Buffer resource over rows [0, rows) of a row-major tensor that starts at
+// `base`, rows `stride_bytes` apart and `row_bytes` long.  Raw buffer loads
+// check each access against the record count and return zeros past it, so
+// tile loaders need no branch for rows beyond the end: row r >= rows starts
+// at r * stride_bytes >= (rows - 1) * stride_bytes + row_bytes.  Offsets are
+// 32-bit, so callers rebase the resource at each tile and keep a tile within
+// 2 GiB (the library bounds row strides).
+constexpr int kBufferDword3 = 0x00020000;  // 32-bit data format (gfx9 encoding)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows,
+                                                            int64_t stride_bytes, int row_bytes) {
+  int64_t n = rows > 0 ? (int64_t)(rows - 1) * stride_bytes + row_bytes : 0;
+  n = n < 0xffffffffll ? n : 0xffffffffll;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
+                                           kBufferDword3);
+}
+__device__ __forceinline__ bf16x8 buffer_load_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // The hardware dispatches workgroup i of a launch to XCD i % 8.  Renumber
 // so that each XCD runs a contiguous range of logical workgroups: logical
 // neighbours (tiles of one head) then share that XCD's L2.

@@ -85,7 +85,8 @@ void fwd_bf16_kernel(FwdArgs a) {
   constexpr int PF = fwd_prefetch<D>();
   __shared__ __attribute__((aligned(16))) bf16 lds[4 * L::tile];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, g = lane >> 5;
 
   const int nqb = (a.Nq + BM - 1) / BM;
@@ -107,35 +108,44 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   const int q0 = qblk * BM + w * QW;
   const bool wave_active = q0 < a.Nq;
-  const bf16x8 zero8 = {};
 
   // this wave's query rows as B operands: lane -> row q0 + 32 qb + ln,
-  // d = 16 kc + 8 g .. +7
+  // d = 16 kc + 8 g .. +7 (rows past Nq read as zeros)
   bf16x8 qreg[NQB][KC];
+  {
+    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, a.Nq - q0, 2 * a.qs.sn, 2 * D);
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qrow = q0 + 32 * qb + ln;
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      qreg[qb][kc] = qrow < a.Nq ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g)
-                                 : zero8;
+      for (int kc = 0; kc < KC; ++kc)
+        qreg[qb][kc] = buffer_load_bf16x8(
+            rq, (uint32_t)((32 * qb + ln) * 2 * a.qs.sn + 2 * (16 * kc + 8 * g)));
   }
 
   // Tile loader with two register sets.  With PF = 2, tile t goes global ->
   // set t % 2 (issued two tiles ahead) -> LDS buffer t % 2 (stored one tile
   // ahead), so each load has two tiles of work to land; with PF = 1 the load
   // is issued one tile ahead.  Piece e -> row e / (D/8), 16-byte column piece
-  // e % (D/8).
+  // e % (D/8).  The loads are unconditional buffer loads (rows past the end
+  // come back as zeros), so no branch separates a load from its use and the
+  // waits before the LDS stores cover only the tile being stored.
+  uint32_t koff[PT], voff[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = tid + u * NT;
+    const int r = e / (D / 8), cc = e % (D / 8);
+    koff[u] = (uint32_t)(r * 2 * a.ks.sn + 16 * cc);
+    voff[u] = (uint32_t)(r * 2 * a.vs.sn + 16 * cc);
+  }
   bf16x8 pk[2][PT], pv[2][PT];
   auto load_tile = [&](auto set_tag, int j0) {
     constexpr int S = decltype(set_tag)::value;
+    const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int e = tid + u * NT;
-      const int r = e / (D / 8), cc = e % (D / 8);
-      const bool ok = e < CH && j0 + r < n_kv;
-      pk[S][u] = ok ? load_bf16x8(kp + (int64_t)(j0 + r) * a.ks.sn + 8 * cc) : zero8;
-      pv[S][u] = ok ? load_bf16x8(vp + (int64_t)(j0 + r) * a.vs.sn + 8 * cc) : zero8;
+      pk[S][u] = buffer_load_bf16x8(rk, koff[u]);
+      pv[S][u] = buffer_load_bf16x8(rv, voff[u]);
     }
   };
   auto store_tile = [&](auto set_tag, int buf) {
@@ -145,7 +155,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
-      if (e < CH) {
+      if (CH % NT == 0 || e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
         *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[S][u];
         *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[S][u];
@@ -169,21 +179,22 @@ void fwd_bf16_kernel(FwdArgs a) {
   const float sl2 = a.scale * kLog2e;
   const float lazy = kLazy / sl2;  // threshold in raw score units
 
-  if (ntiles > 0) {
-    load_tile(S0{}, 0);
-    store_tile(S0{}, 0);
-  }
-  if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
-  __syncthreads();
-
-  // One key/value tile.  MASKED is set only for the ragged last tile, so the
-  // full tiles carry no masking code at all.
-  // With PF = 1 a single register set is used (load and store sets 0) and
-  // the LDS buffer alternates at run time.
-  auto tile = [&](auto masked_tag, auto load_set, auto store_set, int it, int buf) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // One key/value tile.  In the steady state (TAIL false) the caller
+  // guarantees that tile it + PF exists to be loaded and tile it + 1 to be
+  // stored, and that tile it is full: the body then has no condition, no
+  // masking and no branch between loads and their waits.  The last tiles
+  // (TAIL true) test both at run time and mask keys past the end.
+  // With PF = 2 the register set SET = it % 2 receives tile it + 2 and LDS
+  // buffer SET is read; with PF = 1 a single register set is used and the
+  // buffer alternates at run time.
+  auto tile = [&](auto tail_tag, auto set_tag, int it) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    constexpr int SET = decltype(set_tag)::value;
+    using LoadSet = std::integral_constant<int, PF == 2 ? SET : 0>;
+    using StoreSet = std::integral_constant<int, PF == 2 ? 1 - SET : 0>;
+    const int buf = PF == 2 ? SET : (it & 1);
     const int j0 = it * BN;
-    if (it + PF < ntiles) load_tile(load_set, j0 + PF * BN);
+    if (!TAIL || it + PF < ntiles) load_tile(LoadSet{}, j0 + PF * BN);
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
@@ -231,7 +242,7 @@ void fwd_bf16_kernel(FwdArgs a) {
         }
         prio_valu();
       }
-      if constexpr (MASKED) {  // keys past the end weigh nothing
+      if constexpr (TAIL) {  // keys past the end weigh nothing
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -301,31 +312,32 @@ void fwd_bf16_kernel(FwdArgs a) {
       }
       prio_valu();
     }
-    if (it + 1 < ntiles) store_tile(store_set, buf ^ 1);
+    if (!TAIL || it + 1 < ntiles) store_tile(StoreSet{}, buf ^ 1);
     __syncthreads();
   };
-  const int nfull = n_kv / BN;
-  int it = 0;
-  if constexpr (PF == 2) {
-    // SET = it % 2: the LDS buffer read now and the register set receiving
-    // tile it + 2; the other set holds tile it + 1
-    for (; it + 1 < nfull; it += 2) {
-      tile(std::false_type{}, S0{}, S1{}, it, 0);
-      tile(std::false_type{}, S1{}, S0{}, it + 1, 1);
+  // (an empty key range skips the loop; the wait bookkeeping of the loop
+  // then only ever sees the prologue's loads completed)
+  if (ntiles > 0) {
+    load_tile(S0{}, 0);
+    store_tile(S0{}, 0);
+    if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
+    __syncthreads();
+    int it = 0;
+    if constexpr (PF == 2) {
+      // steady state: tiles it and it + 1 both have a tile to prefetch
+      for (; it + 3 < ntiles; it += 2) {
+        tile(std::false_type{}, S0{}, it);
+        tile(std::false_type{}, S1{}, it + 1);
+      }
+      // the last two or three tiles; `it` is even here
+      for (; it < ntiles; it += 2) {
+        tile(std::true_type{}, S0{}, it);
+        if (it + 1 < ntiles) tile(std::true_type{}, S1{}, it + 1);
+      }
+    } else {
+      for (; it + 1 < ntiles; ++it) tile(std::false_type{}, S0{}, it);
+      tile(std::true_type{}, S0{}, it);
     }
-    if (it < nfull) {
-      tile(std::false_type{}, S0{}, S1{}, it, 0);
-      ++it;
-    }
-    if (it < ntiles) {  // the ragged last tile, in whichever set it falls
-      if (it & 1)
-        tile(std::true_type{}, S1{}, S0{}, it, 1);
-      else
-        tile(std::true_type{}, S0{}, S1{}, it, 0);
-    }
-  } else {
-    for (; it < nfull; ++it) tile(std::false_type{}, S0{}, S0{}, it, it & 1);
-    if (it < ntiles) tile(std::true_type{}, S0{}, S0{}, it, it & 1);
   }
 
   if (!wave_active) return;
@@ -410,7 +422,8 @@ void fwd_sp_kernel(FwdArgs a) {
   bf16* const Kslot = lds;                  // [3][tile]
   bf16* const Vslot = lds + 3 * L::tile;    // [2][tile]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, g = lane >> 5;
 
   const int nqb = (a.Nq + BM - 1) / BM;
@@ -697,7 +710,8 @@ void fwd_pp_kernel(FwdArgs a) {
   bf16* const Kslot = lds;                  // [2][tile]
   bf16* const Vslot = lds + 2 * L::tile;    // [2][tile]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, g = lane >> 5;
   const int grp = EXATTN_PP_GROUP_BY_HALF ? (w >> 2) : (w & 1);
 

@@ -61,7 +61,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 /* A [B, H, N, d] tensor: element (b, h, n, c) lives at
  * ptr + (b*sb + h*sh + n*sn + c) elements.  ptr must be 16-byte aligned and
  * sn, sh, sb multiples of 8 (BF16) or 4 (F32) elements, so that a row of d
- * values can be moved with 16-byte vector accesses. */
+ * values can be moved with 16-byte vector accesses.  The row stride sn may
+ * span at most 16 MiB (tiles are addressed with 32-bit offsets); larger
+ * strides are ATTN_E_UNSUPPORTED. */
 typedef struct {
   void* ptr;
   int32_t dtype;           /* attn_dtype */

@@ -86,6 +86,7 @@ def test_fwd_validation(lib):
     assert fwd(lib, v=T(sn=68)) == UNSUPPORTED          # bf16 row stride not a multiple of 8
     assert fwd(lib, o=T(sh=-64)) == INVALID
     assert fwd(lib, lse=FAKE + 2) == UNSUPPORTED
+    assert fwd(lib, k=T(sn=(1 << 23) + 8)) == UNSUPPORTED  # row stride above 16 MiB
 
 
 def test_fwd_chunked_validation(lib):
