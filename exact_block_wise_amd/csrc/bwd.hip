@@ -77,6 +77,14 @@ struct DkdvLds {
   static constexpr int bytes = n_bf16 * 2 + 2 * 2 * bwdk::BM * 4;  // + (LSE, D) x 2
 };
 
+// query tiles in flight per workgroup: two where the second register set
+// fits without spilling
+#ifndef EXATTN_DKDV_PF2
+#define EXATTN_DKDV_PF2 1
+#endif
+template <int D, int KW>
+constexpr int dkdv_prefetch() { return EXATTN_DKDV_PF2 && D <= 64 && KW == 32 ? 2 : 1; }
+
 template <int D, int KW>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   using namespace bwdk;
@@ -143,24 +151,27 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     qoff[u] = (uint32_t)(r * 2 * a.qs.sn + 16 * cc);
     doff[u] = (uint32_t)(r * 2 * a.dos.sn + 16 * cc);
   }
-  bf16x8 pq[PT], pd[PT];
-  float pst = 0.f;
-  auto load_tile = [&](int q0) {
+  constexpr int PF = dkdv_prefetch<D, KW>();
+  bf16x8 pq[2][PT], pd[2][PT];
+  float pst[2] = {0.f, 0.f};
+  auto load_tile = [&](auto set_tag, int q0) {
+    constexpr int S = decltype(set_tag)::value;
     const int rows = a.Nq - q0;
     const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
     const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      pq[u] = buffer_load_bf16x8(rq, qoff[u]);
-      pd[u] = buffer_load_bf16x8(rd, doff[u]);
+      pq[S][u] = buffer_load_bf16x8(rq, qoff[u]);
+      pd[S][u] = buffer_load_bf16x8(rd, doff[u]);
     }
     // threads 0 .. BM-1: LSE (log2 units) of query q0 + tid; BM .. 2BM-1: D
     const int r = tid & (BM - 1);
     const float l = buffer_load_f32(rows_rsrc(lsep + q0, rows, 4, 4), 4 * r);
     const float dd = buffer_load_f32(rows_rsrc(dsp + q0, rows, 4, 4), 4 * r);
-    pst = tid < BM ? (r < rows ? l * kLog2e : INFINITY) : dd;
+    pst[S] = tid < BM ? (r < rows ? l * kLog2e : INFINITY) : dd;
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto set_tag, int buf) {
+    constexpr int S = decltype(set_tag)::value;
     bf16* Qs = lds + buf * 2 * L::tile;
     bf16* dOs = Qs + L::tile;
 #pragma unroll
@@ -168,11 +179,11 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       const int e = tid + u * NT;
       if (CH % NT == 0 || e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
-        *reinterpret_cast<bf16x8*>(&Qs[r * RS + 8 * cc]) = pq[u];
-        *reinterpret_cast<bf16x8*>(&dOs[r * RS + 8 * cc]) = pd[u];
+        *reinterpret_cast<bf16x8*>(&Qs[r * RS + 8 * cc]) = pq[S][u];
+        *reinterpret_cast<bf16x8*>(&dOs[r * RS + 8 * cc]) = pd[S][u];
       }
     }
-    if (tid < 2 * BM) stats[buf * 2 * BM + tid] = pst;
+    if (tid < 2 * BM) stats[buf * 2 * BM + tid] = pst[S];
   };
 
   f32x16 dk[NCB][NDB], dv[NCB][NDB];
@@ -275,10 +286,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 
   // One query tile; NEXT: tile it + 1 exists (its loads are issued before
   // and stored after this tile's work, without a run-time test).
-  auto tile = [&](auto next_tag, int it) {
-    constexpr bool NEXT = decltype(next_tag)::value;
-    const int buf = it & 1;
-    if (NEXT) load_tile((it + 1) * BM);
+  auto tile = [&](auto tail_tag, auto set_tag, int it) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    constexpr int SET = decltype(set_tag)::value;
+    using LoadSet = std::integral_constant<int, PF == 2 ? SET : 0>;
+    using StoreSet = std::integral_constant<int, PF == 2 ? 1 - SET : 0>;
+    const int buf = PF == 2 ? SET : (it & 1);
+    if (!TAIL || it + PF < nqt) load_tile(LoadSet{}, (it + PF) * BM);
     if (wave_active) {
       const bf16* Qs = lds + buf * 2 * L::tile;
       const bf16* dOs = Qs + L::tile;
@@ -356,15 +370,29 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
         prio_valu();
       }
     }
-    if (NEXT) store_tile(buf ^ 1);
+    if (!TAIL || it + 1 < nqt) store_tile(StoreSet{}, buf ^ 1);
     __syncthreads();
   };
-  load_tile(0);
-  store_tile(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load_tile(S0{}, 0);
+  store_tile(S0{}, 0);
+  if (PF == 2 && nqt > 1) load_tile(S1{}, BM);
   __syncthreads();
   int it = 0;
-  for (; it + 1 < nqt; ++it) tile(std::true_type{}, it);
-  tile(std::false_type{}, it);
+  if constexpr (PF == 2) {
+    for (; it + 3 < nqt; it += 2) {
+      tile(std::false_type{}, S0{}, it);
+      tile(std::false_type{}, S1{}, it + 1);
+    }
+    for (; it < nqt; it += 2) {
+      tile(std::true_type{}, S0{}, it);
+      if (it + 1 < nqt) tile(std::true_type{}, S1{}, it + 1);
+    }
+  } else {
+    for (; it + 1 < nqt; ++it) tile(std::false_type{}, S0{}, it);
+    tile(std::true_type{}, S0{}, it);
+  }
 
   if (!wave_active) return;
   if constexpr (kPinAcc) agpr_results_ready();
@@ -405,6 +433,11 @@ namespace dqk {
 constexpr int BN = 64;
 constexpr int NT = 256;
 }  // namespace dqk
+
+// key/value tiles in flight per workgroup (a second register set, 2, fits
+// at d = 64 but measured no faster there)
+template <int D>
+constexpr int dq_prefetch() { return 1; }
 
 template <int D>
 struct DqLds {
@@ -483,17 +516,22 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     koff[u] = (uint32_t)(r * 2 * a.ks.sn + 16 * cc);
     voff[u] = (uint32_t)(r * 2 * a.vs.sn + 16 * cc);
   }
-  bf16x8 pk[PT], pv[PT];
-  auto load_tile = [&](int j0) {
+  // two register sets where they fit: tile t is loaded into set t % 2 two
+  // tiles ahead and stored to LDS buffer t % 2 one tile ahead
+  constexpr int PF = dq_prefetch<D>();
+  bf16x8 pk[2][PT], pv[2][PT];
+  auto load_tile = [&](auto set_tag, int j0) {
+    constexpr int S = decltype(set_tag)::value;
     const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
     const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      pk[u] = buffer_load_bf16x8(rk, koff[u]);
-      pv[u] = buffer_load_bf16x8(rv, voff[u]);
+      pk[S][u] = buffer_load_bf16x8(rk, koff[u]);
+      pv[S][u] = buffer_load_bf16x8(rv, voff[u]);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto set_tag, int buf) {
+    constexpr int S = decltype(set_tag)::value;
     bf16* Kt = lds + buf * 2 * L::tile;
     bf16* Vt = Kt + L::tile;
 #pragma unroll
@@ -501,11 +539,13 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       const int e = tid + u * NT;
       if (CH % NT == 0 || e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
-        *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[u];
-        *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[u];
+        *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[S][u];
+        *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[S][u];
       }
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   f32x16 dq[NQB][NDB];
 #pragma unroll
@@ -514,16 +554,31 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     for (int db = 0; db < NDB; ++db) dq[qb][db] = f32x16{};
   const float sl2 = a.scale * kLog2e;
 
-  // One key/value tile; NEXT: tile it + 1 exists (loaded before and stored
-  // after this tile's work, without a run-time test).
-  auto tile = [&](auto next_tag, int it) {
-    constexpr bool NEXT = decltype(next_tag)::value;
-    const int buf = it & 1;
-    if (NEXT) load_tile((it + 1) * BN);
+  // One key/value tile.  In the steady state (TAIL false) tile it + PF is
+  // loaded and tile it + 1 stored without a run-time test; the last tiles
+  // test both.  With PF = 2 the register set SET = it % 2 receives tile
+  // it + 2 and LDS buffer SET is read; with PF = 1 one set is used and the
+  // buffer alternates at run time.
+  auto tile = [&](auto tail_tag, auto set_tag, int it) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    constexpr int SET = decltype(set_tag)::value;
+    using LoadSet = std::integral_constant<int, PF == 2 ? SET : 0>;
+    using StoreSet = std::integral_constant<int, PF == 2 ? 1 - SET : 0>;
+    const int buf = PF == 2 ? SET : (it & 1);
+    if (!TAIL || it + PF < ntiles) load_tile(LoadSet{}, (it + PF) * BN);
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
       f32x16 st[2][NQB], dpt[2][NQB];
+      // the tile's K and V operands (A operands of S^T and dP^T)
+      bf16x8 ka[2][KC], va[2][KC];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          ka[cb][kc] = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+          va[cb][kc] = load_bf16x8(&Vt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+        }
       prio_mfma();
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
@@ -534,12 +589,10 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
         }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
-          const bf16x8 va = load_bf16x8(&Vt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) {
-            st[cb][qb] = mfma32(ka, qreg[qb][kc], st[cb][qb]);
-            dpt[cb][qb] = mfma32(va, doreg[qb][kc], dpt[cb][qb]);
+            st[cb][qb] = mfma32(ka[cb][kc], qreg[qb][kc], st[cb][qb]);
+            dpt[cb][qb] = mfma32(va[cb][kc], doreg[qb][kc], dpt[cb][qb]);
           }
         }
       }
@@ -570,15 +623,27 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       }
       prio_valu();
     }
-    if (NEXT) store_tile(buf ^ 1);
+    if (!TAIL || it + 1 < ntiles) store_tile(StoreSet{}, buf ^ 1);
     __syncthreads();
   };
-  load_tile(0);
-  store_tile(0);
+  load_tile(S0{}, 0);
+  store_tile(S0{}, 0);
+  if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
   __syncthreads();
   int it = 0;
-  for (; it + 1 < ntiles; ++it) tile(std::true_type{}, it);
-  tile(std::false_type{}, it);
+  if constexpr (PF == 2) {
+    for (; it + 3 < ntiles; it += 2) {
+      tile(std::false_type{}, S0{}, it);
+      tile(std::false_type{}, S1{}, it + 1);
+    }
+    for (; it < ntiles; it += 2) {
+      tile(std::true_type{}, S0{}, it);
+      if (it + 1 < ntiles) tile(std::true_type{}, S1{}, it + 1);
+    }
+  } else {
+    for (; it + 1 < ntiles; ++it) tile(std::false_type{}, S0{}, it);
+    tile(std::true_type{}, S0{}, it);
+  }
 
   if (!wave_active) return;
   // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block

@@ -52,6 +52,7 @@ namespace fwdk {
 constexpr int BN = 64;
 constexpr int NT = 256;
 constexpr float kLazy = 8.0f;  // log2 of the largest weight allowed before rescaling
+constexpr float kSumCap = 256.0f;  // 2^kLazy
 }  // namespace fwdk
 
 template <int D>
@@ -62,9 +63,10 @@ struct FwdLds {
   static constexpr int bytes = 4 * tile * 2;        // K, V x double buffer
 };
 
-// Issue each tile's LDS operand reads in bulk ahead of their products.
-#ifndef EXATTN_FWD_STAGED
-#define EXATTN_FWD_STAGED 0
+// Weigh each tile against the running reference first and take the exact
+// row maximum only when the weights come out too large (see the tile body).
+#ifndef EXATTN_FWD_SUMCHECK
+#define EXATTN_FWD_SUMCHECK 0
 #endif
 
 // Prefetch depth in tiles: two where the second register set fits.
@@ -198,36 +200,10 @@ void fwd_bf16_kernel(FwdArgs a) {
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
-      // S^T = K Q^T for two 32-key blocks x NQB query blocks
       f32x16 s[2][NQB];
-      bf16x8 va[4][NDB];
-      if constexpr (EXATTN_FWD_STAGED) {
-        // all K operand reads first, then the products; the V operands are
-        // read next so that they land while the softmax runs
-        bf16x8 ka[2][KC];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            ka[cb][kc] = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka[cb][kc], qreg[qb][kc], s[cb][qb]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            va[t][db] = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
+      // S^T = K Q^T for two 32-key blocks x NQB query blocks; keys past the
+      // end weigh nothing
+      auto scores = [&]() {
         prio_mfma();
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
@@ -241,32 +217,41 @@ void fwd_bf16_kernel(FwdArgs a) {
           }
         }
         prio_valu();
-      }
-      if constexpr (TAIL) {  // keys past the end weigh nothing
+        if constexpr (TAIL) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+          for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const bool dead = j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3) >= n_kv;
+            for (int e = 0; e < 16; ++e) {
+              const bool dead = j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3) >= n_kv;
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              if (dead) s[cb][qb][e] = -INFINITY;
-          }
-      }
-      // row maxima; raise the reference only when it is exceeded by > 2^8
-      bool raise = false;
-      float mx[NQB];
+              for (int qb = 0; qb < NQB; ++qb)
+                if (dead) s[cb][qb][e] = -INFINITY;
+            }
+        }
+      };
+      // P = exp2(sl2 (s - mref)) in place, and this lane's sum of its 32
+      // weights per query block.  The sum is taken over the fp32 weights: a
+      // peaky row's few dominant weights would carry their bf16 rounding
+      // into the LSE.
+      auto weights = [&](float* psum) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float m = s[0][qb][0];
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float moff = mref[qb] * sl2;
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+          for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) m = fmaxf(m, s[cb][qb][e]);
-        mx[qb] = max_halves(m);
-        raise |= mx[qb] > mref[qb] + lazy;
-      }
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+            for (int e = 0; e < 16; ++e) {
+              const float p = fast_exp2(fmaf(s[cb][qb][e], sl2, -moff));
+              s[cb][qb][e] = p;
+              part[e & 3] += p;
+            }
+          psum[qb] = (part[0] + part[1]) + (part[2] + part[3]);
+        }
+      };
+      // raise the reference to the rows' maxima over this tile (when higher),
+      // rescaling what O and l hold so far
+      auto raise_reference = [&](const float* mx) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const float mnew = fmaxf(mref[qb], mx[qb]);
@@ -276,26 +261,56 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
         }
+      };
+      auto row_max = [&](float* mx) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float m = s[0][qb][0];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, s[cb][qb][e]);
+          mx[qb] = max_halves(m);
+        }
+      };
+      float psum[NQB], mx[NQB];
+      scores();
+      if constexpr (EXATTN_FWD_SUMCHECK) {
+        // Optimistic: weigh against the current reference and check the
+        // lane sums afterwards.  A sum within 2^kLazy bounds every weight by
+        // 2^kLazy; a larger sum (or inf / NaN: the reference is -inf before
+        // the first tile) sends the wave through the exact path once: the
+        // scores are recomputed, the reference is raised to their maximum
+        // and the weights are taken again.  This drops the per-tile row
+        // maximum from the common path.
+        weights(psum);
+        bool low = false;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) low |= !(psum[qb] <= kSumCap);
+        if (__builtin_amdgcn_ballot_w64(low)) {
+          // re-read K from LDS rather than keep the fast path's operands live
+          asm volatile("" ::: "memory");
+          scores();
+          row_max(mx);
+          raise_reference(mx);
+          weights(psum);
+        }
+      } else {
+        // row maxima; raise the reference only when it is exceeded by > 2^8
+        row_max(mx);
+        bool raise = false;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) raise |= mx[qb] > mref[qb] + lazy;
+        if (__builtin_amdgcn_ballot_w64(raise)) raise_reference(mx);
+        weights(psum);
       }
-      // P = exp2(sl2 (s - mref)), then O^T += V^T P^T over four 16-key chunks.
-      // Chunk t = 2 cb + hh holds, for slot group g, keys 16t + 4g + (0..3)
-      // and 16t + 8 + 4g + (0..3): accumulator entries 8hh .. 8hh+7 of block cb.
+      // O^T += V^T P^T over four 16-key chunks.  Chunk t = 2 cb + hh holds,
+      // for slot group g, keys 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3):
+      // accumulator entries 8hh .. 8hh+7 of block cb.
       bf16x8 pb[4][NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        const float moff = mref[qb] * sl2;
-        // the row sum is taken over the fp32 weights: a peaky row's few
-        // dominant weights would carry their bf16 rounding into the LSE
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float p = fast_exp2(fmaf(s[cb][qb][e], sl2, -moff));
-            s[cb][qb][e] = p;
-            part[e & 3] += p;
-          }
-        lsum[qb] += (part[0] + part[1]) + (part[2] + part[3]);
+        lsum[qb] += psum[qb];
 #pragma unroll
         for (int t = 0; t < 4; ++t) pb[t][qb] = acc_half_to_bf16(s[t >> 1][qb], t & 1);
       }
@@ -304,10 +319,9 @@ void fwd_bf16_kernel(FwdArgs a) {
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          if constexpr (!EXATTN_FWD_STAGED)
-            va[t][db] = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+          const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = mfma32(va[t][db], pb[t][qb], oacc[db][qb]);
+          for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = mfma32(va, pb[t][qb], oacc[db][qb]);
         }
       }
       prio_valu();
@@ -447,28 +461,29 @@ void fwd_sp_kernel(FwdArgs a) {
   const int q0 = qblk * BM + w * QW;
   const bool wave_active = q0 < a.Nq;
   const int qrow = q0 + ln;
-  const bf16x8 zero8 = {};
-
   bf16x8 qreg[KC];
+  {
+    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, a.Nq - q0, 2 * a.qs.sn, 2 * D);
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    qreg[kc] = qrow < a.Nq ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g) : zero8;
+    for (int kc = 0; kc < KC; ++kc)
+      qreg[kc] = buffer_load_bf16x8(rq, (uint32_t)(ln * 2 * a.qs.sn + 2 * (16 * kc + 8 * g)));
+  }
 
+  // unconditional buffer loads of a tile's rows (rows past the end are zero)
   bf16x8 pk[PT], pv[PT];
   auto load_rows = [&](const bf16* base, int64_t sn, int j0, bf16x8* dst) {
+    const auto r = rows_rsrc(base + (int64_t)j0 * sn, n_kv - j0, 2 * sn, 2 * D);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
-      const int r = e / (D / 8), cc = e % (D / 8);
-      dst[u] = (e < CH && j0 + r < n_kv) ? load_bf16x8(base + (int64_t)(j0 + r) * sn + 8 * cc)
-                                         : zero8;
+      dst[u] = buffer_load_bf16x8(r, (uint32_t)((e / (D / 8)) * 2 * sn + 16 * (e % (D / 8))));
     }
   };
   auto store_rows = [&](bf16* slot, const bf16x8* src) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
-      if (e < CH) {
+      if (CH % NT == 0 || e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
         *reinterpret_cast<bf16x8*>(&slot[r * KS + 8 * cc]) = src[u];
       }
@@ -521,30 +536,15 @@ void fwd_sp_kernel(FwdArgs a) {
     for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
   };
 
-  // prologue: K_0, K_1, V_0 in LDS; S_0 and its reference maximum
-  if (ntiles > 0) {
-    load_rows(kp, a.ks.sn, 0, pk);
-    store_rows(Kslot, pk);
-    load_rows(vp, a.vs.sn, 0, pv);
-    store_rows(Vslot, pv);
-  }
-  if (ntiles > 1) {
-    load_rows(kp, a.ks.sn, BN, pk);
-    store_rows(Kslot + L::tile, pk);
-  }
-  __syncthreads();
-  if (wave_active && ntiles > 0) {
-    scores(0, scur);
-    if (ntiles == 1 && ragged) mask(0, scur);
-    raise_ref(rowmax(scur));
-  }
-
-  // iteration j; NEXT: tile j + 1 exists, MASKN: it is the ragged last tile
-  auto iteration = [&](auto next_tag, auto maskn_tag, int j) {
+  // iteration j; NEXT: tile j + 1 exists, MASKN: it is the ragged last tile;
+  // TAIL: K_{j+2} / V_{j+1} may not exist (tested at run time), otherwise
+  // both are loaded and stored unconditionally
+  auto iteration = [&](auto next_tag, auto maskn_tag, auto tail_tag, int j) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr bool MASKN = decltype(maskn_tag)::value;
-    if (j + 2 < ntiles) load_rows(kp, a.ks.sn, (j + 2) * BN, pk);
-    if (j + 1 < ntiles) load_rows(vp, a.vs.sn, (j + 1) * BN, pv);
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    if (!TAIL || j + 2 < ntiles) load_rows(kp, a.ks.sn, (j + 2) * BN, pk);
+    if (!TAIL || j + 1 < ntiles) load_rows(vp, a.vs.sn, (j + 1) * BN, pv);
     if (wave_active) {
       // step a: S_{j+1} || softmax of S_j.  The K operands are read first,
       // so that the products need no LDS wait once they start.
@@ -618,20 +618,39 @@ void fwd_sp_kernel(FwdArgs a) {
         for (int cb = 0; cb < 2; ++cb) scur[cb] = snxt[cb];
       }
     }
-    if (j + 2 < ntiles) store_rows(Kslot + ((j + 2) % 3) * L::tile, pk);
-    if (j + 1 < ntiles) store_rows(Vslot + ((j + 1) & 1) * L::tile, pv);
+    if (!TAIL || j + 2 < ntiles) store_rows(Kslot + ((j + 2) % 3) * L::tile, pk);
+    if (!TAIL || j + 1 < ntiles) store_rows(Vslot + ((j + 1) & 1) * L::tile, pv);
     __syncthreads();
   };
-  int j = 0;
-  for (; j + 2 < ntiles; ++j) iteration(std::true_type{}, std::false_type{}, j);
-  if (j + 1 < ntiles) {
-    if (ragged)
-      iteration(std::true_type{}, std::true_type{}, j);
-    else
-      iteration(std::true_type{}, std::false_type{}, j);
-    ++j;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (ntiles > 0) {
+    // prologue: K_0, K_1, V_0 in LDS; S_0 and its reference maximum
+    load_rows(kp, a.ks.sn, 0, pk);
+    store_rows(Kslot, pk);
+    load_rows(vp, a.vs.sn, 0, pv);
+    store_rows(Vslot, pv);
+    if (ntiles > 1) {
+      load_rows(kp, a.ks.sn, BN, pk);
+      store_rows(Kslot + L::tile, pk);
+    }
+    __syncthreads();
+    if (wave_active) {
+      scores(0, scur);
+      if (ntiles == 1 && ragged) mask(0, scur);
+      raise_ref(rowmax(scur));
+    }
+    int j = 0;
+    for (; j + 2 < ntiles; ++j) iteration(T_{}, F_{}, F_{}, j);
+    if (j + 1 < ntiles) {
+      if (ragged)
+        iteration(T_{}, T_{}, T_{}, j);
+      else
+        iteration(T_{}, F_{}, T_{}, j);
+      ++j;
+    }
+    iteration(F_{}, F_{}, T_{}, j);
   }
-  if (j < ntiles) iteration(std::false_type{}, std::false_type{}, j);
 
   if (!wave_active) return;
   const float l = sum_halves(lsum);
