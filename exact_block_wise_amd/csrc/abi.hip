@@ -56,6 +56,14 @@ size_t dsum_bytes(const attn_problem* p) {
   return round_up((size_t)p->B * p->H * p->Nq * sizeof(float), kWsAlign);
 }
 
+// fp32 dQ partials of a split key range (see dq_key_splits), after D
+size_t dq_part_bytes(const attn_problem* p, uint32_t flags) {
+  if (flags & ATTN_BWD_NO_DQ) return 0;
+  const int splits = dq_key_splits(p->B, p->H, p->Nq, p->Nkv);
+  if (splits <= 1) return 0;
+  return round_up((size_t)splits * p->B * p->H * p->Nq * p->d * sizeof(float), kWsAlign);
+}
+
 // o / dout dtypes the preprocess serves: dout BF16 with o BF16 or F32;
 // dout F32 with o F32
 bool pre_dtypes_ok(int o_dtype, int do_dtype) {
@@ -147,9 +155,8 @@ attn_status attn_lse_merge(int32_t n_parts, int32_t B, int32_t H, int32_t Nq, in
 }
 
 size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags) {
-  (void)flags;
   if (check_problem(p) != ATTN_OK) return 0;
-  return dsum_bytes(p);
+  return dsum_bytes(p) + dq_part_bytes(p, flags);
 }
 
 attn_status attn_bwd_preprocess(const attn_problem* p, attn_tensor o, attn_tensor dout,
@@ -194,7 +201,8 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_t
   if (do_dq && (acc ? dq.dtype != ATTN_F32 : dq.dtype != dt)) return ATTN_E_INVALID;
   if (!lse) return ATTN_E_INVALID;
   if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
-  if (!workspace || workspace_bytes < dsum_bytes(p)) return ATTN_E_WORKSPACE;
+  const size_t part_bytes = dq_part_bytes(p, flags);
+  if (!workspace || workspace_bytes < dsum_bytes(p) + part_bytes) return ATTN_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return ATTN_E_WORKSPACE;
 
   BwdArgs a{};
@@ -204,6 +212,11 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_t
   a.dos = strides_of(dout); a.dqs = strides_of(dq); a.dks = strides_of(dk);
   a.dvs = strides_of(dv);
   a.dsum = static_cast<float*>(workspace);
+  a.dq_part = part_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    dsum_bytes(p))
+                         : nullptr;
+  a.dq_splits = 1;
+  a.dq_split_len = p->Nkv;
   a.B = p->B; a.H = p->H; a.Nq = p->Nq; a.Nkv = p->Nkv;
   a.scale = p->scale;
   a.o_f32 = o.dtype == ATTN_F32;

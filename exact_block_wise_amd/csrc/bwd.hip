@@ -9,6 +9,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 #include <math.h>
@@ -17,10 +18,6 @@
 // pin the dK/dV accumulators of one-wave-per-SIMD instances in AGPRs
 #ifndef EXATTN_PIN_ACC
 #define EXATTN_PIN_ACC 1
-#endif
-// interleave two key blocks per wave (64 key rows) with scheduling hints
-#ifndef EXATTN_DKDV_PIPE
-#define EXATTN_DKDV_PIPE 0
 #endif
 
 namespace exattn {
@@ -77,6 +74,123 @@ struct DkdvLds {
   static constexpr int bytes = n_bf16 * 2 + 2 * 2 * bwdk::BM * 4;  // + (LSE, D) x 2
 };
 
+// One 32-query block against a wave's NCB x 32 keys: S = Q K^T and
+// dP = dO V^T (queries as A operands, the wave's K / V rows as B operands),
+// P = exp2(S log2e scale - LSE2), dS = P (dP - D), then dV += P^T dO and
+// dK += dS^T Q with the accumulator halves as A operands and the dO / Q
+// columns from LDS transpose reads.  Qs / dOs: row-major bf16 query rows
+// (row stride rs), lse2s / Ds: their LSE in log2 units and D.
+template <int D, int NCB, bool PIN>
+__device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int rs,
+                                            const float* lse2s, const float* Ds, int nb,
+                                            float sl2, const bf16x8 (&kreg)[NCB][D / 16],
+                                            const bf16x8 (&vreg)[NCB][D / 16],
+                                            f32x16 (&dk)[NCB][(D + 31) / 32],
+                                            f32x16 (&dv)[NCB][(D + 31) / 32], int lane) {
+  constexpr int KC = D / 16, NDB = (D + 31) / 32;
+  const int ln = lane & 31, g = lane >> 5;
+  bf16x8 qa[KC], da[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    qa[kc] = load_bf16x8(&Qs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
+    da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
+  }
+  f32x16 s[NCB], dp[NCB];
+  prio_mfma();
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    s[cb] = f32x16{};
+    dp[cb] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      s[cb] = mfma32(qa[kc], kreg[cb][kc], s[cb]);
+      dp[cb] = mfma32(da[kc], vreg[cb][kc], dp[cb]);
+    }
+  }
+  prio_valu();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = 32 * nb + 8 * i + 4 * g;
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[qi]);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(s[cb][4 * i + r], sl2, -l4[r]));
+        s[cb][4 * i + r] = p;
+        dp[cb][4 * i + r] = p * (dp[cb][4 * i + r] - d4[r]);
+      }
+  }
+  // dV^T += dO^T P, dK^T += Q^T dS over two 16-query chunks t = 2 nb + hh:
+  // slot group g holds queries 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3).
+  // The dO / Q columns (LDS transpose reads) are the A operands and the
+  // accumulator halves of P and dS the B operands, so the gradients come
+  // out transposed: a lane owns one key and runs of 4 consecutive d, which
+  // leave in 8-byte stores.
+  prio_mfma();
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int t = 2 * nb + hh;
+    bf16x8 pa[NCB], sa[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      pa[cb] = acc_half_to_bf16(s[cb], hh);
+      sa[cb] = acc_half_to_bf16(dp[cb], hh);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const bf16x8 dob = tr_operand(dOs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+      const bf16x8 qbv = tr_operand(Qs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        if constexpr (PIN) {
+          mfma32_agpr(dob, pa[cb], dv[cb][db]);
+          mfma32_agpr(qbv, sa[cb], dk[cb][db]);
+        } else {
+          dv[cb][db] = mfma32(dob, pa[cb], dv[cb][db]);
+          dk[cb][db] = mfma32(qbv, sa[cb], dk[cb][db]);
+        }
+      }
+    }
+  }
+  prio_valu();
+}
+
+// dK (scaled) and dV of a wave's keys kw .. kw + 32 NCB - 1 from the
+// transposed accumulators: lane owns key kw + 32cb + ln and, per 32-column
+// block db, the runs d = 32db + 8i + 4g + (0..3) (accumulator entries
+// 4i .. 4i+3), each written as one 8-byte store.
+template <int D, int NCB>
+__device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, int kw,
+                                           const f32x16 (&dk)[NCB][(D + 31) / 32],
+                                           const f32x16 (&dv)[NCB][(D + 31) / 32], int lane) {
+  constexpr int NDB = (D + 31) / 32;
+  const int ln = lane & 31, g = lane >> 5;
+  bf16* dkp = (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh;
+  bf16* dvp = (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int kr = kw + 32 * cb + ln;
+    if (kr >= a.Nkv) continue;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * g;
+        if (d0 >= D) continue;
+        const f32x16& k16 = dk[cb][db];
+        const f32x16& v16 = dv[cb][db];
+        const bf16x4 k4 = {(bf16)(k16[4 * i] * a.scale), (bf16)(k16[4 * i + 1] * a.scale),
+                           (bf16)(k16[4 * i + 2] * a.scale), (bf16)(k16[4 * i + 3] * a.scale)};
+        const bf16x4 v4 = {(bf16)v16[4 * i], (bf16)v16[4 * i + 1], (bf16)v16[4 * i + 2],
+                           (bf16)v16[4 * i + 3]};
+        *reinterpret_cast<bf16x4*>(dkp + (int64_t)kr * a.dks.sn + d0) = k4;
+        *reinterpret_cast<bf16x4*>(dvp + (int64_t)kr * a.dvs.sn + d0) = v4;
+      }
+  }
+}
+
 // query tiles in flight per workgroup: two where the second register set
 // fits without spilling
 #ifndef EXATTN_DKDV_PF2
@@ -94,8 +208,6 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   // pin dK/dV in AGPRs only in the one-wave-per-SIMD instances, where the
   // registers fit without spilling (see mfma32_agpr)
   constexpr bool kPinAcc = EXATTN_PIN_ACC && (KW == 64 || D > 80);
-  // explicit MFMA / VALU interleaving of two key blocks (builtin products)
-  constexpr bool kPipe = EXATTN_DKDV_PIPE && !kPinAcc;
   constexpr int BN = 4 * KW;                   // key rows per workgroup
   constexpr int CH = BM * (D / 8);             // 16-byte pieces per Q (or dO) tile
   constexpr int PT = (CH + NT - 1) / NT;
@@ -197,93 +309,6 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const float sl2 = a.scale * kLog2e;
   const int nqt = (a.Nq + BM - 1) / BM;
 
-  // Two key blocks per wave, arranged so that the matrix work of one block
-  // overlaps the elementwise work of the other inside the wave:
-  //   S/dP(cb0) | S/dP(cb1) + P,dS(cb0) | dV/dK(cb0) + P,dS(cb1) | dV/dK(cb1)
-  // The sched_group_barrier hints ask the scheduler to alternate one matrix
-  // instruction with a few vector instructions in the overlapped phases.
-  auto pipelined_block = [&](const bf16* Qs, const bf16* dOs, const float* lse2s,
-                             const float* Ds, int nb) {
-    bf16x8 qa[KC], da[KC];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      qa[kc] = load_bf16x8(&Qs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
-      da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
-    }
-    f32x4 l4[4], d4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qi = 32 * nb + 8 * i + 4 * g;
-      l4[i] = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
-      d4[i] = *reinterpret_cast<const f32x4*>(&Ds[qi]);
-    }
-    auto sdp = [&](int cb, f32x16& s_, f32x16& dp_) {
-      s_ = f32x16{};
-      dp_ = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        s_ = mfma32(qa[kc], kreg[cb][kc], s_);
-        dp_ = mfma32(da[kc], vreg[cb][kc], dp_);
-      }
-    };
-    auto elementwise = [&](f32x16& s_, f32x16& dp_) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(s_[4 * i + r], sl2, -l4[i][r]));
-          s_[4 * i + r] = p;
-          dp_[4 * i + r] = p * (dp_[4 * i + r] - d4[i][r]);
-        }
-    };
-    // transposed B operands (dO and Q columns) for both 16-query chunks
-    bf16x8 dob[2][NDB], qbv[2][NDB];
-    auto load_tr = [&]() {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int t = 2 * nb + hh;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dob[hh][db] = tr_operand(dOs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
-          qbv[hh][db] = tr_operand(Qs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
-        }
-      }
-    };
-    auto dvdk = [&](int cb, const f32x16& p_, const f32x16& ds_) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8 pa = acc_half_to_bf16(p_, hh);
-        const bf16x8 sa = acc_half_to_bf16(ds_, hh);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[cb][db] = mfma32(pa, dob[hh][db], dv[cb][db]);
-          dk[cb][db] = mfma32(sa, qbv[hh][db], dk[cb][db]);
-        }
-      }
-    };
-    f32x16 s0, dp0, s1, dp1;
-    sdp(0, s0, dp0);
-    load_tr();
-    __builtin_amdgcn_sched_barrier(0);
-    sdp(1, s1, dp1);
-    elementwise(s0, dp0);
-#pragma unroll
-    for (int k = 0; k < 2 * KC; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix op
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight vector ops
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    dvdk(0, s0, dp0);
-    elementwise(s1, dp1);
-#pragma unroll
-    for (int k = 0; k < 4 * NDB; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    dvdk(1, s1, dp1);
-  };
-
   // One query tile; NEXT: tile it + 1 exists (its loads are issued before
   // and stored after this tile's work, without a run-time test).
   auto tile = [&](auto tail_tag, auto set_tag, int it) {
@@ -301,74 +326,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       // one 32-row query block at a time keeps the live registers of a block
       // (its S, dP and operands) from being doubled by interleaving
 #pragma unroll 1
-      for (int nb = 0; nb < BM / 32; ++nb) {
-        if constexpr (NCB == 2 && kPipe) {
-          pipelined_block(Qs, dOs, lse2s, Ds, nb);
-          continue;
-        }
-        bf16x8 qa[KC], da[KC];
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          qa[kc] = load_bf16x8(&Qs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
-          da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * RS + 16 * kc + 8 * g]);
-        }
-        f32x16 s[NCB], dp[NCB];
-        prio_mfma();
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          s[cb] = f32x16{};
-          dp[cb] = f32x16{};
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            s[cb] = mfma32(qa[kc], kreg[cb][kc], s[cb]);
-            dp[cb] = mfma32(da[kc], vreg[cb][kc], dp[cb]);
-          }
-        }
-        prio_valu();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qi = 32 * nb + 8 * i + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[qi]);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float p = fast_exp2(fmaf(s[cb][4 * i + r], sl2, -l4[r]));
-              s[cb][4 * i + r] = p;
-              dp[cb][4 * i + r] = p * (dp[cb][4 * i + r] - d4[r]);
-            }
-        }
-        // dV += P^T dO, dK += dS^T Q over two 16-query chunks t = 2 nb + hh:
-        // slot group g holds queries 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3)
-        prio_mfma();
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int t = 2 * nb + hh;
-          bf16x8 pa[NCB], sa[NCB];
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            pa[cb] = acc_half_to_bf16(s[cb], hh);
-            sa[cb] = acc_half_to_bf16(dp[cb], hh);
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 dob = tr_operand(dOs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
-            const bf16x8 qbv = tr_operand(Qs + 32 * db, RS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-              if constexpr (kPinAcc) {
-                mfma32_agpr(pa[cb], dob, dv[cb][db]);
-                mfma32_agpr(sa[cb], qbv, dk[cb][db]);
-              } else {
-                dv[cb][db] = mfma32(pa[cb], dob, dv[cb][db]);
-                dk[cb][db] = mfma32(sa[cb], qbv, dk[cb][db]);
-              }
-            }
-          }
-        }
-        prio_valu();
-      }
+      for (int nb = 0; nb < BM / 32; ++nb)
+        dkdv_qblock<D, NCB, kPinAcc>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
     }
     if (!TAIL || it + 1 < nqt) store_tile(StoreSet{}, buf ^ 1);
     __syncthreads();
@@ -396,24 +355,135 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 
   if (!wave_active) return;
   if constexpr (kPinAcc) agpr_results_ready();
-  // dK (scaled) and dV: lane owns column d = 32db + ln, key rows 8i+4g+r
-  bf16* dkp = (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh;
-  bf16* dvp = (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh;
+  dkdv_store<D, NCB>(a, b, h, kw, dk, dv, lane);
+}
+
+// --------------------------------------------------------------------------
+// bf16 dK / dV for a short query block against a long key range
+// (Nq <= 128, e.g. a query block attending to a long video or image-token
+// cache, as in the cross-attention setting of "LV-XAttn", section 3).
+//
+// The whole query side (Q, dO, LSE, D: at most 128 rows) is loaded into LDS
+// once per workgroup and stays there.  The workgroup then walks its share of
+// the head's 128-key blocks; each wave owns 32 keys of a block, holds their
+// K / V rows in registers, and loads the rows of its next block while it
+// computes the current one (so the key stream overlaps the matrix work).
+// No barrier is needed inside the key loop: the query side is read-only and
+// each wave's keys are its own.  dK and dV leave as each block completes.
+// --------------------------------------------------------------------------
+namespace resk {
+constexpr int QR = 128;  // resident query rows
+constexpr int NT = 256;
+constexpr int KB = 128;  // keys per workgroup step (4 waves x 32)
+}  // namespace resk
+
+template <int D>
+struct ResLds {
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int RS = DP + 8;                           // row stride of Q, dO
+  static constexpr int bytes = 2 * resk::QR * RS * 2 + 2 * resk::QR * 4;
+};
+
+#ifndef EXATTN_DKDV_RESIDENT
+#define EXATTN_DKDV_RESIDENT 1
+#endif
+
+template <int D>
+__global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int groups) {
+  using namespace resk;
+  using L = ResLds<D>;
+  constexpr int KC = D / 16, NDB = (D + 31) / 32, RS = L::RS;
+  constexpr bool kPin = EXATTN_PIN_ACC && D > 80;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* const Qs = reinterpret_cast<bf16*>(smem);
+  bf16* const dOs = Qs + QR * RS;
+  float* const lse2s = reinterpret_cast<float*>(dOs + QR * RS);
+  float* const Ds = lse2s + QR;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int ln = lane & 31, g = lane >> 5;
+
+  int idx = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = idx % groups;
+  idx /= groups;
+  const int h = idx % a.H;
+  const int b = idx / a.H;
+
+  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
+  const bf16* dop = (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh;
+  const float* lsep = a.lse + ((int64_t)b * a.H + h) * a.Nq;
+  const float* dsp = a.dsum + ((int64_t)b * a.H + h) * a.Nq;
+
+  // the query side; rows past Nq are zero with LSE = +inf (P = 0)
+  {
+    constexpr int PT = QR * (D / 8) / NT;  // 16-byte pieces per thread and tensor
+    const auto rq = rows_rsrc(qp, a.Nq, 2 * a.qs.sn, 2 * D);
+    const auto rd = rows_rsrc(dop, a.Nq, 2 * a.dos.sn, 2 * D);
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int dcol = 32 * db + ln;
-      if (dcol >= D) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kr = kw + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (kr < a.Nkv) {
-          dkp[(int64_t)kr * a.dks.sn + dcol] = (bf16)(dk[cb][db][e] * a.scale);
-          dvp[(int64_t)kr * a.dvs.sn + dcol] = (bf16)dv[cb][db][e];
-        }
-      }
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * NT;
+      const int r = e / (D / 8), cc = e % (D / 8);
+      const bf16x8 vq = buffer_load_bf16x8(rq, (uint32_t)(r * 2 * a.qs.sn + 16 * cc));
+      const bf16x8 vd = buffer_load_bf16x8(rd, (uint32_t)(r * 2 * a.dos.sn + 16 * cc));
+      *reinterpret_cast<bf16x8*>(&Qs[r * RS + 8 * cc]) = vq;
+      *reinterpret_cast<bf16x8*>(&dOs[r * RS + 8 * cc]) = vd;
     }
+    const int r = tid & (QR - 1);
+    const float l = buffer_load_f32(rows_rsrc(lsep, a.Nq, 4, 4), 4 * r);
+    const float dd = buffer_load_f32(rows_rsrc(dsp, a.Nq, 4, 4), 4 * r);
+    if (tid < QR)
+      lse2s[r] = r < a.Nq ? l * kLog2e : INFINITY;
+    else
+      Ds[r] = dd;
+  }
+  __syncthreads();
+
+  const int nkb = (a.Nkv + KB - 1) / KB;
+  const int nqb = (a.Nq + 31) / 32;
+  const float sl2 = a.scale * kLog2e;
+  int kb = grp;
+  if (kb >= nkb) return;  // the whole workgroup; no barrier follows
+
+  // this wave's 32 keys of block kb_ as B operands (rows past Nkv: zero)
+  auto load_kv = [&](int kb_, bf16x8 (&kr)[1][KC], bf16x8 (&vr)[1][KC]) {
+    const int kw = kb_ * KB + 32 * w;
+    const auto rk = rows_rsrc(kp + (int64_t)kw * a.ks.sn, a.Nkv - kw, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)kw * a.vs.sn, a.Nkv - kw, 2 * a.vs.sn, 2 * D);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int col = 2 * (16 * kc + 8 * g);
+      kr[0][kc] = buffer_load_bf16x8(rk, (uint32_t)(ln * 2 * a.ks.sn + col));
+      vr[0][kc] = buffer_load_bf16x8(rv, (uint32_t)(ln * 2 * a.vs.sn + col));
+    }
+  };
+  bf16x8 kreg[1][KC], vreg[1][KC], knext[1][KC], vnext[1][KC];
+  f32x16 dk[1][NDB], dv[1][NDB];
+  auto block = [&](int kb_) {
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      dk[0][i] = f32x16{};
+      dv[0][i] = f32x16{};
+    }
+#pragma unroll 1
+    for (int nb = 0; nb < nqb; ++nb)
+      dkdv_qblock<D, 1, kPin>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
+    if constexpr (kPin) agpr_results_ready();
+    dkdv_store<D, 1>(a, b, h, kb_ * KB + 32 * w, dk, dv, lane);
+  };
+  load_kv(kb, kreg, vreg);
+  for (; kb + groups < nkb; kb += groups) {
+    load_kv(kb + groups, knext, vnext);
+    block(kb);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      kreg[0][kc] = knext[0][kc];
+      vreg[0][kc] = vnext[0][kc];
+    }
+  }
+  block(kb);
 }
 
 // --------------------------------------------------------------------------
@@ -467,13 +537,16 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   int idx = xcd_remap(blockIdx.x, gridDim.x);
   const int qblk = idx % nqb;
   idx /= nqb;
+  const int split = idx % a.dq_splits;   // key range [split * len, ...)
+  idx /= a.dq_splits;
   const int h = idx % a.H;
   const int b = idx / a.H;
+  const int kv_lo = split * a.dq_split_len;
 
   const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
   const bf16* dop = (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh;
-  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh;
-  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh + (int64_t)kv_lo * a.ks.sn;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh + (int64_t)kv_lo * a.vs.sn;
   const float* lsep = a.lse + ((int64_t)b * a.H + h) * a.Nq;
   const float* dsp = a.dsum + ((int64_t)b * a.H + h) * a.Nq;
 
@@ -505,7 +578,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     }
   }
 
-  const int n_kv = a.Nkv;
+  const int n_kv = min(a.Nkv - kv_lo, a.dq_split_len);
   const int ntiles = (n_kv + BN - 1) / BN;
   // key/value tile loader: unconditional buffer loads, rows past Nkv zero
   uint32_t koff[PT], voff[PT];
@@ -658,7 +731,9 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
         const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
         if (qr >= a.Nq) continue;
         const float v = dq[qb][db][e] * a.scale;
-        if (accumulate) {
+        if (a.dq_splits > 1) {  // this key range's share, summed by dq_reduce_kernel
+          a.dq_part[((((int64_t)split * a.B + b) * a.H + h) * a.Nq + qr) * D + dcol] = v;
+        } else if (accumulate) {
           float* p = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)qr * a.dqs.sn + dcol;
           *p += v;
         } else {
@@ -667,6 +742,50 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
         }
       }
     }
+}
+
+// --------------------------------------------------------------------------
+// dQ over split key ranges: dQ = sum over ranges of the partials, in range
+// order (so the result does not depend on scheduling), then written in dQ's
+// dtype or added to an fp32 dQ.  One thread per 4 consecutive d.
+// --------------------------------------------------------------------------
+template <typename TO>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a, int d, int accumulate) {
+  const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int dv4 = d / 4;
+  if (i >= rows * dv4) return;
+  const int64_t row = i / dv4;
+  const int c = 4 * (int)(i % dv4);
+  f32x4 acc = *reinterpret_cast<const f32x4*>(a.dq_part + row * d + c);
+  for (int sp = 1; sp < a.dq_splits; ++sp)
+    acc += *reinterpret_cast<const f32x4*>(a.dq_part + (sp * rows + row) * d + c);
+  const int q = (int)(row % a.Nq);
+  const int64_t bh = row / a.Nq;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int64_t o = b * a.dqs.sb + h * a.dqs.sh + (int64_t)q * a.dqs.sn + c;
+  if constexpr (sizeof(TO) == 4) {
+    f32x4* p = reinterpret_cast<f32x4*>((float*)a.dq + o);
+    *p = accumulate ? *p + acc : acc;
+  } else {
+    const bf16x4 v = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+    *reinterpret_cast<bf16x4*>((bf16*)a.dq + o) = v;
+  }
+}
+
+// Query blocks per dQ workgroup are 128 rows; below this many workgroups the
+// key range is split (each range at least 8 key tiles of 64).
+constexpr long long kDqTargetWorkgroups = 1024;
+
+int dq_key_splits(int B, int H, int Nq, int Nkv) {
+  const long long base = (long long)((Nq + 127) / 128) * H * B;
+  const int ntiles = (Nkv + dqk::BN - 1) / dqk::BN;
+  if (base >= kDqTargetWorkgroups) return 1;
+  int s = (int)((kDqTargetWorkgroups + base - 1) / base);
+  s = min(s, ntiles / 8);
+  if (s < 2) return 1;
+  const int per = (ntiles + s - 1) / s;  // tiles per range; every range non-empty
+  return (ntiles + per - 1) / per;
 }
 
 // Occupancy: kernels whose registers fit request two waves per SIMD.
@@ -872,8 +991,13 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t s) {
 }
 
 template <int D, int QW, bool W2>
-static hipError_t launch_dq(const BwdArgs& a, int accumulate, hipStream_t s) {
-  const long long grid = (long long)((a.Nq + 4 * QW - 1) / (4 * QW)) * a.H * a.B;
+static hipError_t launch_dq(const BwdArgs& a_in, int accumulate, hipStream_t s) {
+  BwdArgs a = a_in;
+  const int ntiles = (a.Nkv + dqk::BN - 1) / dqk::BN;
+  a.dq_splits = a.dq_part ? dq_key_splits(a.B, a.H, a.Nq, a.Nkv) : 1;
+  a.dq_split_len = ((ntiles + a.dq_splits - 1) / a.dq_splits) * dqk::BN;
+  const long long grid =
+      (long long)((a.Nq + 4 * QW - 1) / (4 * QW)) * a.H * a.B * a.dq_splits;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const int lds = DqLds<D>::bytes;
   if constexpr (W2) {
@@ -887,6 +1011,47 @@ static hipError_t launch_dq(const BwdArgs& a, int accumulate, hipStream_t s) {
     hipLaunchKernelGGL((dq_bf16_kernel<D, QW>), dim3((unsigned)grid), dim3(dqk::NT), lds, s, a,
                        accumulate);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.dq_splits == 1) return e;
+  const long long n4 = (long long)a.B * a.H * a.Nq * (D / 4);
+  const unsigned rg = (unsigned)((n4 + 255) / 256);
+  if (accumulate)
+    hipLaunchKernelGGL((dq_reduce_kernel<float>), dim3(rg), dim3(256), 0, s, a, D, 1);
+  else
+    hipLaunchKernelGGL((dq_reduce_kernel<bf16>), dim3(rg), dim3(256), 0, s, a, D, 0);
+  return hipGetLastError();
+}
+
+static int compute_units() {
+  static const int n = [] {
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu <= 0)
+      return 256;
+    return cu;
+  }();
+  return n;
+}
+
+// resident query side: at most 128 query rows and at least 4 key blocks
+static bool use_resident_dkdv(const BwdArgs& a) {
+  return EXATTN_DKDV_RESIDENT && a.Nq <= resk::QR && (a.Nkv + resk::KB - 1) / resk::KB >= 4;
+}
+
+template <int D>
+static hipError_t launch_dkdv_resident(const BwdArgs& a, hipStream_t s) {
+  const long long nkb = (a.Nkv + resk::KB - 1) / resk::KB;
+  const long long heads = (long long)a.B * a.H;
+  // about one workgroup per compute unit, each walking a share of its head
+  const long long groups = std::min(nkb, std::max(1LL, (compute_units() + heads - 1) / heads));
+  const long long grid = heads * groups;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int lds = ResLds<D>::bytes;
+  static const hipError_t attr = allow_lds(&dkdv_resident_kernel<D>, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((dkdv_resident_kernel<D>), dim3((unsigned)grid), dim3(resk::NT), lds, s, a,
+                     (int)groups);
   return hipGetLastError();
 }
 
@@ -894,7 +1059,8 @@ template <int D, int KW, int QW, bool W2>
 static hipError_t bwd_bf16_d(const BwdArgs& a, int do_dkdv, int do_dq, int accumulate,
                              hipStream_t s) {
   if (do_dkdv) {
-    const hipError_t e = launch_dkdv<D, KW>(a, s);
+    const hipError_t e =
+        use_resident_dkdv(a) ? launch_dkdv_resident<D>(a, s) : launch_dkdv<D, KW>(a, s);
     if (e != hipSuccess) return e;
   }
   if (do_dq) return launch_dq<D, QW, W2>(a, accumulate, s);

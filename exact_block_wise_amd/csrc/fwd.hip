@@ -750,29 +750,31 @@ void fwd_pp_kernel(FwdArgs a) {
   const int q0 = qblk * BM + w * QW;
   const bool wave_active = q0 < a.Nq;
   const int qrow = q0 + ln;
-  const bf16x8 zero8 = {};
 
   bf16x8 qreg[KC];
+  {
+    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, a.Nq - q0, 2 * a.qs.sn, 2 * D);
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    qreg[kc] = qrow < a.Nq ? load_bf16x8(qp + (int64_t)qrow * a.qs.sn + 16 * kc + 8 * g) : zero8;
+    for (int kc = 0; kc < KC; ++kc)
+      qreg[kc] = buffer_load_bf16x8(rq, (uint32_t)(ln * 2 * a.qs.sn + 2 * (16 * kc + 8 * g)));
+  }
 
-  // prefetch registers for one (K_{t+1}, V_t) pair
+  // prefetch registers for one (K_{t+1}, V_t) pair; unconditional buffer
+  // loads (rows past the end are zero)
   bf16x8 pk[PT], pv[PT];
   auto load_rows = [&](const bf16* base, int64_t sn, int j0, bf16x8* dst) {
+    const auto r = rows_rsrc(base + (int64_t)j0 * sn, n_kv - j0, 2 * sn, 2 * D);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
-      const int r = e / (D / 8), cc = e % (D / 8);
-      dst[u] = (e < CH && j0 + r < n_kv) ? load_bf16x8(base + (int64_t)(j0 + r) * sn + 8 * cc)
-                                         : zero8;
+      dst[u] = buffer_load_bf16x8(r, (uint32_t)((e / (D / 8)) * 2 * sn + 16 * (e % (D / 8))));
     }
   };
   auto store_rows = [&](bf16* slot, const bf16x8* src) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int e = tid + u * NT;
-      if (e < CH) {
+      if (CH % NT == 0 || e < CH) {
         const int r = e / (D / 8), cc = e % (D / 8);
         *reinterpret_cast<bf16x8*>(&slot[r * KS + 8 * cc]) = src[u];
       }
@@ -788,17 +790,10 @@ void fwd_pp_kernel(FwdArgs a) {
   const float sl2 = a.scale * kLog2e;
   const float lazy = fwdk::kLazy / sl2;
 
-  // prologue: K_0 into slot 0; the pair (K_1, V_0) into registers
-  load_rows(kp, a.ks.sn, 0, pk);
-  store_rows(Kslot, pk);
-  load_rows(kp, a.ks.sn, BN, pk);
-  load_rows(vp, a.vs.sn, 0, pv);
-  __syncthreads();
-
-  // matrix phase M(j): S_j (if j < ntiles) and PV of tile j - 1 (if j >= 1)
-  auto mphase = [&](int j) {
-    if (j < ntiles) {
-      const bf16* Kt = Kslot + (j & 1) * L::tile;
+  // matrix phase M(t): S_t (when t < ntiles) and PV of tile t - 1 (t >= 1)
+  auto mphase = [&](int t) __attribute__((always_inline)) {
+    if (t < ntiles) {
+      const bf16* Kt = Kslot + (t & 1) * L::tile;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         s[cb] = f32x16{};
@@ -809,20 +804,20 @@ void fwd_pp_kernel(FwdArgs a) {
         }
       }
     }
-    if (j >= 1) {
-      const bf16* Vt = Vslot + ((j - 1) & 1) * L::tile;
+    if (t >= 1) {
+      const bf16* Vt = Vslot + ((t - 1) & 1) * L::tile;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
-          oacc[db] = mfma32(va, pb[t], oacc[db]);
+          const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * u + 4 * g, 16 * u + 8 + 4 * g, lane);
+          oacc[db] = mfma32(va, pb[u], oacc[db]);
         }
     }
   };
-  // vector phase V(j): P_j from S_j
-  auto vphase = [&](int j) {
-    const int j0 = j * BN;
+  // vector phase V(t): P_t from S_t (keys past the end masked)
+  auto vphase = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * BN;
     if (j0 + BN > n_kv) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
@@ -856,30 +851,51 @@ void fwd_pp_kernel(FwdArgs a) {
       }
     lsum += (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pb[t] = acc_half_to_bf16(s[t >> 1], t & 1);
+    for (int u = 0; u < 4; ++u) pb[u] = acc_half_to_bf16(s[u >> 1], u & 1);
   };
 
-  // phase p of a group: even -> M(p / 2), odd -> V((p - 1) / 2); 2 ntiles + 1
-  // phases per group, group 1 one step behind group 0
-  const int nphase = 2 * ntiles + 1;
-  for (int step = 0; step < nphase + 1; ++step) {
-    if ((step & 1) == 0) {
-      // pair t = step / 2: store (K_{t+1}, V_t), then load the next pair
-      const int t = step >> 1;
-      if (t + 1 < ntiles) store_rows(Kslot + ((t + 1) & 1) * L::tile, pk);
-      if (t < ntiles) store_rows(Vslot + (t & 1) * L::tile, pv);
-      if (t + 2 < ntiles) load_rows(kp, a.ks.sn, (t + 2) * BN, pk);
-      if (t + 1 < ntiles) load_rows(vp, a.vs.sn, (t + 1) * BN, pv);
-    }
-    const int p = step - grp;
-    if (wave_active && p >= 0 && p < nphase) {
-      if ((p & 1) == 0)
-        mphase(p >> 1);
-      else
-        vphase(p >> 1);
+  // Step pair t: the even step stores the pair (K_{t+1}, V_t) loaded one pair
+  // earlier and loads (K_{t+2}, V_{t+1}); group 0 runs M(t) then V(t),
+  // group 1 runs V(t - 1) then M(t), so on every SIMD one wave multiplies
+  // while the other exponentiates.  In the steady state (TAIL false) all
+  // four tiles exist and every phase runs; the last pairs test at run time.
+  const bool g0 = grp == 0;
+  auto pair = [&](auto tail_tag, int t) __attribute__((always_inline)) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    if (!TAIL || t + 1 < ntiles) store_rows(Kslot + ((t + 1) & 1) * L::tile, pk);
+    if (!TAIL || t < ntiles) store_rows(Vslot + (t & 1) * L::tile, pv);
+    if (!TAIL || t + 2 < ntiles) load_rows(kp, a.ks.sn, (t + 2) * BN, pk);
+    if (!TAIL || t + 1 < ntiles) load_rows(vp, a.vs.sn, (t + 1) * BN, pv);
+    if (wave_active) {
+      if (g0) {
+        if (!TAIL || t <= ntiles) mphase(t);
+      } else {
+        if (!TAIL || (t >= 1 && t - 1 < ntiles)) vphase(t - 1);
+      }
     }
     __syncthreads();
-  }
+    if (wave_active) {
+      if (g0) {
+        if (!TAIL || t < ntiles) vphase(t);
+      } else {
+        if (!TAIL || t <= ntiles) mphase(t);
+      }
+    }
+    __syncthreads();
+  };
+
+  // prologue: K_0 into its slot, the pair (K_1, V_0) into registers
+  load_rows(kp, a.ks.sn, 0, pk);
+  store_rows(Kslot, pk);
+  load_rows(kp, a.ks.sn, BN, pk);
+  load_rows(vp, a.vs.sn, 0, pv);
+  __syncthreads();
+  // pair 0 has no V(-1) / PV(-1); pairs 1 .. ntiles - 3 are the steady
+  // state; the rest (through pair ntiles, which only finishes PV) are tails
+  pair(std::true_type{}, 0);
+  int t = 1;
+  for (; t + 2 < ntiles; ++t) pair(std::false_type{}, t);
+  for (; t <= ntiles; ++t) pair(std::true_type{}, t);
 
   if (!wave_active) return;
   const float l = sum_halves(lsum);

@@ -38,10 +38,13 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsum;   // [B,H,Nq] contiguous: D_i = dO_i . O_i
+  float* dq_part;  // [dq_splits,B,H,Nq,d] fp32 partials (dq_splits > 1)
   Strides qs, ks, vs, os, dos, dqs, dks, dvs;
   int B, H, Nq, Nkv;
   float scale;
   int o_f32;     // o dtype is fp32
+  int dq_splits;     // key ranges the dQ pass is split into (1: none)
+  int dq_split_len;  // keys per range, a multiple of the key tile
 };
 
 struct MergeArgs {
@@ -62,5 +65,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int do_dkdv, int do_dq, int 
 hipError_t launch_bwd_f32(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
                           hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+// Number of key ranges the bf16 dQ pass splits Nkv into (1 = unsplit): a
+// split is used only when the query blocks alone would leave most compute
+// units idle (a short query block against a long key range).
+int dq_key_splits(int B, int H, int Nq, int Nkv);
 
 }  // namespace exattn

@@ -116,6 +116,13 @@ def test_workspace_query(lib):
     for flags in (0, 1, 2, 4, 8):
         assert lib.attn_bwd_workspace_bytes(ctypes.byref(p), flags) == rup(rows * 4)
     assert lib.attn_bwd_workspace_bytes(None, 0) == 0
+    # a short query block against a long key range: the dQ pass is split over
+    # 8 key ranges, whose fp32 partials follow D in the workspace (none when
+    # dQ is not computed)
+    px = P(B=4, H=32, Nq=128, Nkv=32768, d=128)
+    rows_x = 4 * 32 * 128
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(px), 0) == rup(rows_x * 4) + 8 * rows_x * 128 * 4
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(px), 4) == rup(rows_x * 4)
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(P(d=96)), 0) == 0
 
 

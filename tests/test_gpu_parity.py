@@ -58,6 +58,8 @@ SMALL = [
     (1, 1, 1, 1, 64, "bf16", 1.0),         # degenerate: one query, one key
     (1, 2, 33, 1, 64, "bf16", 1.0),        # one key: O = v_1, dQ = dK = 0
     (1, 1, 5, 3000, 64, "bf16", 1.0),      # tiny query block, long keys
+    (1, 2, 100, 1000, 128, "bf16", 1.0),   # resident query block, ragged keys, d = 128
+    (2, 1, 128, 700, 80, "bf16", 1.0),     # resident query block (full), d = 80
     (1, 2, 200, 200, 64, "bf16", 8.0),     # peaky softmax (running max stress)
     (1, 2, 150, 170, 80, "bf16", 8.0),
     (1, 2, 196, 196, 64, "f32", 1.0),
