@@ -79,8 +79,9 @@ struct DkdvLds {
 // P = exp2(S log2e scale - LSE2), dS = P (dP - D), then dV += P^T dO and
 // dK += dS^T Q with the accumulator halves as A operands and the dO / Q
 // columns from LDS transpose reads.  Qs / dOs: row-major bf16 query rows
-// (row stride rs), lse2s / Ds: their LSE in log2 units and D.
-template <int D, int NCB, bool PIN>
+// (row stride rs), lse2s / Ds: their LSE in log2 units (natural log with
+// LSE_NATURAL) and D.
+template <int D, int NCB, bool PIN, bool LSE_NATURAL = false>
 __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int rs,
                                             const float* lse2s, const float* Ds, int nb,
                                             float sl2, const bf16x8 (&kreg)[NCB][D / 16],
@@ -111,7 +112,8 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qi = 32 * nb + 8 * i + 4 * g;
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
+    f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
+    if constexpr (LSE_NATURAL) l4 *= kLog2e;  // staged as stored (natural log)
     const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[qi]);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -191,10 +193,14 @@ __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, int k
   }
 }
 
-// query tiles in flight per workgroup: two where the second register set
-// fits without spilling
+// stage query tiles with direct-to-LDS loads instead of through registers
+#ifndef EXATTN_DKDV_DMA
+#define EXATTN_DKDV_DMA 1
+#endif
+// query tiles in flight per workgroup: a second register set (2) fits at
+// d = 64 only at the edge of spilling and measured no faster there
 #ifndef EXATTN_DKDV_PF2
-#define EXATTN_DKDV_PF2 1
+#define EXATTN_DKDV_PF2 0
 #endif
 template <int D, int KW>
 constexpr int dkdv_prefetch() { return EXATTN_DKDV_PF2 && D <= 64 && KW == 32 ? 2 : 1; }
@@ -298,6 +304,49 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     if (tid < 2 * BM) stats[buf * 2 * BM + tid] = pst[S];
   };
 
+  // Direct-to-LDS staging of the query tiles (no registers, no LDS stores
+  // in the loop).  Wave instruction i of a tensor fills bytes
+  // [1024 i, 1024 (i + 1)) of its tile: lane L the 16-byte chunk 64 i + L,
+  // i.e. row (64 i + L) / CPR, chunk (64 i + L) % CPR of the padded rows
+  // (the last CPR - D/8 chunks of a row are padding; their lanes re-load
+  // chunk 0).  Waves take i = w, w + 4, ...  LSE and D are staged as stored
+  // (natural-log LSE); query rows past Nq read as zero, and with Q = dO = 0
+  // and D = 0 their P is finite and their dS and dO rows are zero, so they
+  // add nothing.
+  constexpr int CPR = RS / 8;
+  constexpr int NI = BM * CPR / 64;
+  constexpr int NIW = (NI + 3) / 4;
+  static_assert(BM * CPR % 64 == 0, "tile must be whole wave instructions");
+  uint32_t qdma[NIW], ddma[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    const int pc = 64 * (w + 4 * j) + lane;
+    const int r = pc / CPR, ch = pc % CPR;
+    const int c = ch < D / 8 ? ch : 0;
+    qdma[j] = (uint32_t)(r * 2 * a.qs.sn + 16 * c);
+    ddma[j] = (uint32_t)(r * 2 * a.dos.sn + 16 * c);
+  }
+  auto load_tile_dma = [&](int q0, int buf) {
+    const int rows = a.Nq - q0;
+    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
+    const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
+    const uint32_t qbase = lds_address(lds + buf * 2 * L::tile);
+    const uint32_t dbase = qbase + 2 * L::tile;
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int i = w + 4 * j;
+      if (NI % 4 == 0 || i < NI) {
+        buffer_load_lds16(rq, qbase + 1024 * i, qdma[j]);
+        buffer_load_lds16(rd, dbase + 1024 * i, ddma[j]);
+      }
+    }
+    const uint32_t sbase = lds_address(stats + buf * 2 * BM);
+    if (w == 0)
+      buffer_load_lds4(rows_rsrc(lsep + q0, rows, 4, 4), sbase, 4 * lane);
+    else if (w == 1)
+      buffer_load_lds4(rows_rsrc(dsp + q0, rows, 4, 4), sbase + 4 * BM, 4 * lane);
+  };
+
   f32x16 dk[NCB][NDB], dv[NCB][NDB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -332,25 +381,54 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     if (!TAIL || it + 1 < nqt) store_tile(StoreSet{}, buf ^ 1);
     __syncthreads();
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  load_tile(S0{}, 0);
-  store_tile(S0{}, 0);
-  if (PF == 2 && nqt > 1) load_tile(S1{}, BM);
-  __syncthreads();
-  int it = 0;
-  if constexpr (PF == 2) {
-    for (; it + 3 < nqt; it += 2) {
-      tile(std::false_type{}, S0{}, it);
-      tile(std::false_type{}, S1{}, it + 1);
-    }
-    for (; it < nqt; it += 2) {
-      tile(std::true_type{}, S0{}, it);
-      if (it + 1 < nqt) tile(std::true_type{}, S1{}, it + 1);
-    }
+  if constexpr (EXATTN_DKDV_DMA) {
+    // one query tile; NEXT: tile it + 1 exists and is staged into the other
+    // buffer while this one is computed (waited for before the barrier)
+    auto tile_dma = [&](auto next_tag, int it) {
+      constexpr bool NEXT = decltype(next_tag)::value;
+      const int buf = it & 1;
+      if (NEXT) load_tile_dma((it + 1) * BM, buf ^ 1);
+      if (wave_active) {
+        const bf16* Qs = lds + buf * 2 * L::tile;
+        const bf16* dOs = Qs + L::tile;
+        const float* lses = stats + buf * 2 * BM;
+        const float* Ds = lses + BM;
+#pragma unroll 1
+        for (int nb = 0; nb < BM / 32; ++nb)
+          dkdv_qblock<D, NCB, kPinAcc, true>(Qs, dOs, RS, lses, Ds, nb, sl2, kreg, vreg, dk, dv,
+                                             lane);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+    load_tile_dma(0, 0);
+    wait_vmem();
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < nqt; ++it) tile_dma(std::true_type{}, it);
+    tile_dma(std::false_type{}, it);
   } else {
-    for (; it + 1 < nqt; ++it) tile(std::false_type{}, S0{}, it);
-    tile(std::true_type{}, S0{}, it);
+  using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    load_tile(S0{}, 0);
+    store_tile(S0{}, 0);
+    if (PF == 2 && nqt > 1) load_tile(S1{}, BM);
+    __syncthreads();
+    int it = 0;
+    if constexpr (PF == 2) {
+      for (; it + 3 < nqt; it += 2) {
+        tile(std::false_type{}, S0{}, it);
+        tile(std::false_type{}, S1{}, it + 1);
+      }
+      for (; it < nqt; it += 2) {
+        tile(std::true_type{}, S0{}, it);
+        if (it + 1 < nqt) tile(std::true_type{}, S1{}, it + 1);
+      }
+    } else {
+      for (; it + 1 < nqt; ++it) tile(std::false_type{}, S0{}, it);
+      tile(std::true_type{}, S0{}, it);
+    }
+  
   }
 
   if (!wave_active) return;

@@ -163,6 +163,31 @@ __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Direct-to-LDS buffer loads: lane L's 16 (or 4) bytes from byte offset
+// `off` of the buffer land at LDS byte address lds + 16 L (4 L), without
+// passing through registers; `lds` must be wave-uniform.  They are written
+// as inline assembly so that the compiler's wait bookkeeping, which cannot
+// tell that a later LDS read of another buffer does not overlap them,
+// inserts no wait: callers must wait_vmem() before the barrier that
+// publishes the data, and must keep no compiler-issued vector-memory load
+// outstanding across them that a wait computed for it would under-count.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds,
+                                                  uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(off), "s"(r) : "memory");
+}
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, uint32_t lds,
+                                                 uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(off), "s"(r) : "memory");
+}
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+}
+
 // The hardware dispatches workgroup i of a launch to XCD i % 8.  Renumber
 // so that each XCD runs a contiguous range of logical workgroups: logical
 // neighbours (tiles of one head) then share that XCD's L2.
