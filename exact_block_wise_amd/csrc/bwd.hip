@@ -305,41 +305,21 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   };
 
   // Direct-to-LDS staging of the query tiles (no registers, no LDS stores
-  // in the loop).  Wave instruction i of a tensor fills bytes
-  // [1024 i, 1024 (i + 1)) of its tile: lane L the 16-byte chunk 64 i + L,
-  // i.e. row (64 i + L) / CPR, chunk (64 i + L) % CPR of the padded rows
-  // (the last CPR - D/8 chunks of a row are padding; their lanes re-load
-  // chunk 0).  Waves take i = w, w + 4, ...  LSE and D are staged as stored
+  // in the loop; see LdsTileDma).  LSE and D are staged as stored
   // (natural-log LSE); query rows past Nq read as zero, and with Q = dO = 0
   // and D = 0 their P is finite and their dS and dO rows are zero, so they
   // add nothing.
-  constexpr int CPR = RS / 8;
-  constexpr int NI = BM * CPR / 64;
-  constexpr int NIW = (NI + 3) / 4;
-  static_assert(BM * CPR % 64 == 0, "tile must be whole wave instructions");
-  uint32_t qdma[NIW], ddma[NIW];
-#pragma unroll
-  for (int j = 0; j < NIW; ++j) {
-    const int pc = 64 * (w + 4 * j) + lane;
-    const int r = pc / CPR, ch = pc % CPR;
-    const int c = ch < D / 8 ? ch : 0;
-    qdma[j] = (uint32_t)(r * 2 * a.qs.sn + 16 * c);
-    ddma[j] = (uint32_t)(r * 2 * a.dos.sn + 16 * c);
-  }
+  LdsTileDma<D, RS, BM> tq, td;
+  tq.init(w, lane, a.qs.sn);
+  td.init(w, lane, a.dos.sn);
   auto load_tile_dma = [&](int q0, int buf) {
     const int rows = a.Nq - q0;
     const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
     const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
     const uint32_t qbase = lds_address(lds + buf * 2 * L::tile);
     const uint32_t dbase = qbase + 2 * L::tile;
-#pragma unroll
-    for (int j = 0; j < NIW; ++j) {
-      const int i = w + 4 * j;
-      if (NI % 4 == 0 || i < NI) {
-        buffer_load_lds16(rq, qbase + 1024 * i, qdma[j]);
-        buffer_load_lds16(rd, dbase + 1024 * i, ddma[j]);
-      }
-    }
+    tq.issue(rq, qbase, w);
+    td.issue(rd, dbase, w);
     const uint32_t sbase = lds_address(stats + buf * 2 * BM);
     if (w == 0)
       buffer_load_lds4(rows_rsrc(lsep + q0, rows, 4, 4), sbase, 4 * lane);
@@ -582,6 +562,10 @@ constexpr int BN = 64;
 constexpr int NT = 256;
 }  // namespace dqk
 
+// stage key/value tiles with direct-to-LDS loads instead of through registers
+#ifndef EXATTN_DQ_DMA
+#define EXATTN_DQ_DMA 1
+#endif
 // key/value tiles in flight per workgroup (a second register set, 2, fits
 // at d = 64 but measured no faster there)
 template <int D>
@@ -705,6 +689,18 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     for (int db = 0; db < NDB; ++db) dq[qb][db] = f32x16{};
   const float sl2 = a.scale * kLog2e;
 
+  // direct-to-LDS staging of the key/value tiles (see LdsTileDma)
+  LdsTileDma<D, KS, BN> tk, tv;
+  tk.init(w, lane, a.ks.sn);
+  tv.init(w, lane, a.vs.sn);
+  auto load_tile_dma = [&](int j0, int buf) {
+    const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
+    const uint32_t kbase = lds_address(lds + buf * 2 * L::tile);
+    tk.issue(rk, kbase, w);
+    tv.issue(rv, kbase + 2 * L::tile, w);
+  };
+
   // One key/value tile.  In the steady state (TAIL false) tile it + PF is
   // loaded and tile it + 1 stored without a run-time test; the last tiles
   // test both.  With PF = 2 the register set SET = it % 2 receives tile
@@ -716,7 +712,11 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     using LoadSet = std::integral_constant<int, PF == 2 ? SET : 0>;
     using StoreSet = std::integral_constant<int, PF == 2 ? 1 - SET : 0>;
     const int buf = PF == 2 ? SET : (it & 1);
-    if (!TAIL || it + PF < ntiles) load_tile(LoadSet{}, (it + PF) * BN);
+    if constexpr (EXATTN_DQ_DMA) {
+      if (!TAIL || it + 1 < ntiles) load_tile_dma((it + 1) * BN, buf ^ 1);
+    } else {
+      if (!TAIL || it + PF < ntiles) load_tile(LoadSet{}, (it + PF) * BN);
+    }
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
@@ -774,15 +774,24 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       }
       prio_valu();
     }
-    if (!TAIL || it + 1 < ntiles) store_tile(StoreSet{}, buf ^ 1);
+    if constexpr (EXATTN_DQ_DMA) {
+      wait_vmem();
+    } else {
+      if (!TAIL || it + 1 < ntiles) store_tile(StoreSet{}, buf ^ 1);
+    }
     __syncthreads();
   };
-  load_tile(S0{}, 0);
-  store_tile(S0{}, 0);
-  if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
+  if constexpr (EXATTN_DQ_DMA) {
+    load_tile_dma(0, 0);
+    wait_vmem();
+  } else {
+    load_tile(S0{}, 0);
+    store_tile(S0{}, 0);
+    if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
+  }
   __syncthreads();
   int it = 0;
-  if constexpr (PF == 2) {
+  if constexpr (PF == 2 && !EXATTN_DQ_DMA) {
     for (; it + 3 < ntiles; it += 2) {
       tile(std::false_type{}, S0{}, it);
       tile(std::false_type{}, S1{}, it + 1);
@@ -881,7 +890,7 @@ __global__ __launch_bounds__(dqk::NT) void dq_bf16_kernel(BwdArgs a, int accumul
   dq_body<D, QW>(a, accumulate);
 }
 template <int D, int QW>
-__global__ __launch_bounds__(dqk::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(dqk::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_bf16_kernel_w2(BwdArgs a, int accumulate) {
   dq_body<D, QW>(a, accumulate);
 }

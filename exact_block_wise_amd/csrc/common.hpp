@@ -188,6 +188,38 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
 }
 
+// Direct-to-LDS staging of a ROWS x D bf16 tile (rows `sn` elements apart
+// in HBM) into a row-padded LDS tile of row stride RS elements: the tile's
+// ROWS * RS / 8 sixteen-byte chunks are written by wave instructions of 64
+// chunks each, instruction i by wave i % 4 of the workgroup; lane L of
+// instruction i carries chunk 64 i + L, i.e. row (64 i + L) / (RS / 8),
+// chunk (64 i + L) % (RS / 8).  Lanes on padding chunks re-load chunk 0 of
+// their row, so no lane is masked off.
+template <int D, int RS, int ROWS>
+struct LdsTileDma {
+  static constexpr int CPR = RS / 8;
+  static constexpr int NI = ROWS * CPR / 64;
+  static constexpr int NIW = (NI + 3) / 4;
+  static_assert(RS % 8 == 0 && RS >= D && ROWS * CPR % 64 == 0,
+                "tile must be whole wave instructions");
+  uint32_t off[NIW];
+  __device__ __forceinline__ void init(int w, int lane, int64_t sn) {
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int pc = 64 * (w + 4 * j) + lane;
+      const int r = pc / CPR, ch = pc % CPR;
+      off[j] = (uint32_t)(r * 2 * sn + 16 * (ch < D / 8 ? ch : 0));
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, uint32_t lds, int w) const {
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int i = w + 4 * j;
+      if (NI % 4 == 0 || i < NI) buffer_load_lds16(r, lds + 1024 * i, off[j]);
+    }
+  }
+};
+
 // The hardware dispatches workgroup i of a launch to XCD i % 8.  Renumber
 // so that each XCD runs a contiguous range of logical workgroups: logical
 // neighbours (tiles of one head) then share that XCD's L2.
