@@ -69,7 +69,13 @@ struct FwdLds {
 #define EXATTN_FWD_SUMCHECK 0
 #endif
 
-// Prefetch depth in tiles: two where the second register set fits.
+// Stage key/value tiles with direct-to-LDS loads (one tile ahead, two LDS
+// buffers) instead of through registers.
+#ifndef EXATTN_FWD_DMA
+#define EXATTN_FWD_DMA 1
+#endif
+// Prefetch depth in tiles when staging through registers: two where the
+// second register set fits.
 template <int D>
 constexpr int fwd_prefetch() { return D <= 80 ? 2 : 1; }
 
@@ -166,6 +172,19 @@ void fwd_bf16_kernel(FwdArgs a) {
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  // direct-to-LDS staging (see LdsTileDma): one tile ahead, no registers
+  LdsTileDma<D, KS, BN> tk, tv;
+  if constexpr (EXATTN_FWD_DMA) {
+    tk.init(w, lane, a.ks.sn);
+    tv.init(w, lane, a.vs.sn);
+  }
+  auto load_tile_dma = [&](int j0, int buf) {
+    const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
+    const uint32_t kbase = lds_address(lds + buf * 2 * L::tile);
+    tk.issue(rk, kbase, w);
+    tv.issue(rv, kbase + 2 * L::tile, w);
+  };
 
   f32x16 oacc[NDB][NQB];
 #pragma unroll
@@ -194,9 +213,15 @@ void fwd_bf16_kernel(FwdArgs a) {
     constexpr int SET = decltype(set_tag)::value;
     using LoadSet = std::integral_constant<int, PF == 2 ? SET : 0>;
     using StoreSet = std::integral_constant<int, PF == 2 ? 1 - SET : 0>;
-    const int buf = PF == 2 ? SET : (it & 1);
+    // two-set register staging: buffer SET; otherwise (one set, or direct
+    // staging) the buffer alternates with the tile
+    const int buf = (PF == 2 && !EXATTN_FWD_DMA) ? SET : (it & 1);
     const int j0 = it * BN;
-    if (!TAIL || it + PF < ntiles) load_tile(LoadSet{}, j0 + PF * BN);
+    if constexpr (EXATTN_FWD_DMA) {
+      if (!TAIL || it + 1 < ntiles) load_tile_dma(j0 + BN, buf ^ 1);
+    } else {
+      if (!TAIL || it + PF < ntiles) load_tile(LoadSet{}, j0 + PF * BN);
+    }
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
@@ -326,18 +351,27 @@ void fwd_bf16_kernel(FwdArgs a) {
       }
       prio_valu();
     }
-    if (!TAIL || it + 1 < ntiles) store_tile(StoreSet{}, buf ^ 1);
+    if constexpr (EXATTN_FWD_DMA) {
+      wait_vmem();
+    } else {
+      if (!TAIL || it + 1 < ntiles) store_tile(StoreSet{}, buf ^ 1);
+    }
     __syncthreads();
   };
   // (an empty key range skips the loop; the wait bookkeeping of the loop
   // then only ever sees the prologue's loads completed)
   if (ntiles > 0) {
-    load_tile(S0{}, 0);
-    store_tile(S0{}, 0);
-    if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
+    if constexpr (EXATTN_FWD_DMA) {
+      load_tile_dma(0, 0);
+      wait_vmem();
+    } else {
+      load_tile(S0{}, 0);
+      store_tile(S0{}, 0);
+      if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
+    }
     __syncthreads();
     int it = 0;
-    if constexpr (PF == 2) {
+    if constexpr (PF == 2 && !EXATTN_FWD_DMA) {
       // steady state: tiles it and it + 1 both have a tile to prefetch
       for (; it + 3 < ntiles; it += 2) {
         tile(std::false_type{}, S0{}, it);
