@@ -885,13 +885,15 @@ __attribute__((amdgpu_waves_per_eu(KW == 32 && D <= 80 ? EXATTN_DKDV_WAVES : 1))
 void dkdv_bf16_kernel(BwdArgs a) {
   dkdv_body<D, KW>(a);
 }
+// Occupancy of the dQ kernel: three waves per SIMD fit d = 64 and d = 80
+// without spills, two fit d = 128.
+#ifndef EXATTN_DQ_WAVES
+#define EXATTN_DQ_WAVES 3
+#endif
 template <int D, int QW>
-__global__ __launch_bounds__(dqk::NT) void dq_bf16_kernel(BwdArgs a, int accumulate) {
-  dq_body<D, QW>(a, accumulate);
-}
-template <int D, int QW>
-__global__ __launch_bounds__(dqk::NT) __attribute__((amdgpu_waves_per_eu(2)))
-void dq_bf16_kernel_w2(BwdArgs a, int accumulate) {
+__global__ __launch_bounds__(dqk::NT)
+__attribute__((amdgpu_waves_per_eu(D <= 80 ? EXATTN_DQ_WAVES : 2)))
+void dq_bf16_kernel(BwdArgs a, int accumulate) {
   dq_body<D, QW>(a, accumulate);
 }
 
@@ -1036,14 +1038,6 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dq_kernel(BwdArgs a, int acc
 // --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
-#ifndef EXATTN_DKDV_KW64
-#define EXATTN_DKDV_KW64 32
-#endif
-
-#ifndef EXATTN_DQ_QW64
-#define EXATTN_DQ_QW64 32
-#endif
-
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, int in_bf16, hipStream_t s) {
   const long long rows = (long long)a.B * a.H * a.Nq;
   const long long grid = (rows + 15) / 16;
@@ -1077,7 +1071,7 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int QW, bool W2>
+template <int D, int QW>
 static hipError_t launch_dq(const BwdArgs& a_in, int accumulate, hipStream_t s) {
   BwdArgs a = a_in;
   const int ntiles = (a.Nkv + dqk::BN - 1) / dqk::BN;
@@ -1087,17 +1081,10 @@ static hipError_t launch_dq(const BwdArgs& a_in, int accumulate, hipStream_t s) 
       (long long)((a.Nq + 4 * QW - 1) / (4 * QW)) * a.H * a.B * a.dq_splits;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const int lds = DqLds<D>::bytes;
-  if constexpr (W2) {
-    static const hipError_t attr = allow_lds(&dq_bf16_kernel_w2<D, QW>, lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((dq_bf16_kernel_w2<D, QW>), dim3((unsigned)grid), dim3(dqk::NT), lds, s, a,
-                       accumulate);
-  } else {
-    static const hipError_t attr = allow_lds(&dq_bf16_kernel<D, QW>, lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((dq_bf16_kernel<D, QW>), dim3((unsigned)grid), dim3(dqk::NT), lds, s, a,
-                       accumulate);
-  }
+  static const hipError_t attr = allow_lds(&dq_bf16_kernel<D, QW>, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((dq_bf16_kernel<D, QW>), dim3((unsigned)grid), dim3(dqk::NT), lds, s, a,
+                     accumulate);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.dq_splits == 1) return e;
   const long long n4 = (long long)a.B * a.H * a.Nq * (D / 4);
@@ -1142,7 +1129,7 @@ static hipError_t launch_dkdv_resident(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int KW, int QW, bool W2>
+template <int D, int KW, int QW>
 static hipError_t bwd_bf16_d(const BwdArgs& a, int do_dkdv, int do_dq, int accumulate,
                              hipStream_t s) {
   if (do_dkdv) {
@@ -1150,18 +1137,16 @@ static hipError_t bwd_bf16_d(const BwdArgs& a, int do_dkdv, int do_dq, int accum
         use_resident_dkdv(a) ? launch_dkdv_resident<D>(a, s) : launch_dkdv<D, KW>(a, s);
     if (e != hipSuccess) return e;
   }
-  if (do_dq) return launch_dq<D, QW, W2>(a, accumulate, s);
+  if (do_dq) return launch_dq<D, QW>(a, accumulate, s);
   return hipSuccess;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
                            hipStream_t s) {
   switch (d) {
-    case 64:
-      return bwd_bf16_d<64, EXATTN_DKDV_KW64, EXATTN_DQ_QW64, EXATTN_DQ_QW64 == 32>(
-          a, do_dkdv, do_dq, accumulate, s);
-    case 80: return bwd_bf16_d<80, 32, 32, true>(a, do_dkdv, do_dq, accumulate, s);
-    case 128: return bwd_bf16_d<128, 32, 32, false>(a, do_dkdv, do_dq, accumulate, s);
+    case 64: return bwd_bf16_d<64, 32, 32>(a, do_dkdv, do_dq, accumulate, s);
+    case 80: return bwd_bf16_d<80, 32, 32>(a, do_dkdv, do_dq, accumulate, s);
+    case 128: return bwd_bf16_d<128, 32, 32>(a, do_dkdv, do_dq, accumulate, s);
   }
   return hipErrorInvalidValue;
 }

@@ -69,6 +69,10 @@ struct FwdLds {
 #define EXATTN_FWD_SUMCHECK 0
 #endif
 
+// Issue a tile's K operand reads in bulk ahead of its score products.
+#ifndef EXATTN_FWD_KSTAGE
+#define EXATTN_FWD_KSTAGE 0
+#endif
 // Stage key/value tiles with direct-to-LDS loads (one tile ahead, two LDS
 // buffers) instead of through registers.
 #ifndef EXATTN_FWD_DMA
@@ -230,15 +234,34 @@ void fwd_bf16_kernel(FwdArgs a) {
       // end weigh nothing
       auto scores = [&]() {
         prio_mfma();
+        if constexpr (EXATTN_FWD_KSTAGE) {
+          // all K operand reads of the tile first, then the products
+          bf16x8 ka[2][KC];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+          for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+            for (int kc = 0; kc < KC; ++kc)
+              ka[cb][kc] = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+          for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
+            for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+              for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka[cb][kc], qreg[qb][kc], s[cb][qb]);
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+              const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+#pragma unroll
+              for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
+            }
           }
         }
         prio_valu();
