@@ -55,7 +55,7 @@ def parse():
 # --------------------------------------------------------------------------
 KERNEL_SOURCES = {"fwd": "fwd.hip", "fwd_chunked": "fwd.hip", "bwd_dkdv": "bwd.hip",
                   "bwd_dq": "bwd.hip"}
-KERNEL_SYMBOLS = {"fwd": "fwd_", "fwd_chunked": "fwd_", "bwd_dkdv": "dkdv_bf16_kernel",
+KERNEL_SYMBOLS = {"fwd": "fwd_", "fwd_chunked": "fwd_", "bwd_dkdv": "dkdv_",
                   "bwd_dq": "dq_bf16_kernel"}
 COPY_BYTES = 1 << 31  # 2 GiB read and 2 GiB written by the calibration copy
 

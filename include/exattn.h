@@ -155,8 +155,13 @@ attn_status attn_lse_merge(int32_t n_parts, int32_t B, int32_t H, int32_t Nq,
 /*
  * attn_bwd_workspace_bytes -- device workspace attn_bwd needs for problem p
  * and the given flags (0 if p is invalid): B*H*Nq floats for D, rounded up
- * to 256 bytes.  The caller allocates it; unless ATTN_BWD_D_PRECOMPUTED is
- * passed its contents on entry do not matter.
+ * to 256 bytes; then, when dQ is computed for a short query block against a
+ * long key range (the dQ pass then splits the keys into ranges so that the
+ * whole GPU is used), the fp32 partials of dQ, ranges*B*H*Nq*d floats
+ * rounded up to 256 bytes.  The size depends on the shape only, not on the
+ * dtype.  The caller allocates it; unless ATTN_BWD_D_PRECOMPUTED is passed
+ * its contents on entry do not matter (the D part is then read; the rest is
+ * always scratch).
  */
 size_t attn_bwd_workspace_bytes(const attn_problem* p, uint32_t flags);
 
