@@ -222,8 +222,12 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_t
   a.o_f32 = o.dtype == ATTN_F32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!pre_done) {
-    const hipError_t e = launch_bwd_pre(a, p->d, dt == ATTN_BF16, s);
-    if (e != hipSuccess) return ATTN_E_HIP;
+    if (do_dq && dt == ATTN_BF16) {
+      a.dq_computes_d = 1;  // the bf16 dQ kernel forms D and runs first
+    } else {
+      const hipError_t e = launch_bwd_pre(a, p->d, dt == ATTN_BF16, s);
+      if (e != hipSuccess) return ATTN_E_HIP;
+    }
   }
   if (dt == ATTN_F32) return from_hip(launch_bwd_f32(a, p->d, do_dkdv, do_dq, acc, s));
   return from_hip(launch_bwd_bf16(a, p->d, do_dkdv, do_dq, acc, s));

@@ -26,6 +26,7 @@ namespace exattn {
 // Preprocess: D_i = sum_c dO_ic O_ic in fp32, one 16-lane group per row.
 // (D_i also equals sum_j P_ij dP_ij, the row term of the softmax Jacobian.)
 // --------------------------------------------------------------------------
+// fp32 dO (and O): one 16-lane group per row.
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int d) {
   const int gi = threadIdx.x >> 4, li = threadIdx.x & 15;
@@ -42,6 +43,47 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int d) {
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
   if (li == 0) a.dsum[row] = acc;
+}
+
+// bf16 dO: D in exactly the order the dQ kernel forms it when it computes D
+// itself (two half-rows d = 16kc + 8g + j, each an fma chain in (kc, j)
+// order, then their sum), so that both routes give the same bits.  Two
+// threads per row.
+template <typename TO>
+__global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(BwdArgs a, int d) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t >> 1;  // over B*H*Nq
+  const int g = (int)(t & 1);
+  const int64_t nrows = (int64_t)a.B * a.H * a.Nq;
+  if (row >= nrows) return;  // both threads of a row leave together
+  const int i = (int)(row % a.Nq);
+  const int64_t bh = row / a.Nq;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const bf16* dop = (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh + (int64_t)i * a.dos.sn;
+  const TO* op = (const TO*)a.o + b * a.os.sb + h * a.os.sh + (int64_t)i * a.os.sn;
+  float acc = 0.f;
+  for (int kc = 0; kc < d / 16; ++kc) {
+    const int c = 16 * kc + 8 * g;
+    const bf16x8 dv8 = load_bf16x8(dop + c);
+    float o8[8];
+    if constexpr (sizeof(TO) == 4) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(op + c);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(op + c + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o8[j] = lo[j];
+        o8[4 + j] = hi[j];
+      }
+    } else {
+      const bf16x8 v = load_bf16x8(reinterpret_cast<const bf16*>(op) + c);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o8[j] = (float)v[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf((float)dv8[j], o8[j], acc);
+  }
+  const float total = acc + __shfl_xor(acc, 1);
+  if (g == 0) a.dsum[row] = total;
 }
 
 // --------------------------------------------------------------------------
@@ -629,14 +671,56 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     for (int qb = 0; qb < NQB; ++qb) {
       const int r = 32 * qb + ln;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int col = 2 * (16 * kc + 8 * g);
-        qreg[qb][kc] = buffer_load_bf16x8(rq, (uint32_t)(r * 2 * a.qs.sn + col));
-        doreg[qb][kc] = buffer_load_bf16x8(rd, (uint32_t)(r * 2 * a.dos.sn + col));
+      for (int kc = 0; kc < KC; ++kc)
+        doreg[qb][kc] = buffer_load_bf16x8(rd, (uint32_t)(r * 2 * a.dos.sn + 2 * (16 * kc + 8 * g)));
+    }
+    if (a.dq_computes_d) {
+      // D_i = dO_i . O_i from the stored O (the backward preprocess, done
+      // here on the rows this wave holds, before its Q rows are loaded);
+      // lanes l and l + 32 hold the two halves of each row's d.  Key range 0
+      // writes D for the dK/dV pass.
+      const int ob = a.o_f32 ? 4 : 2;
+      const char* opb = (const char*)a.o + (b * a.os.sb + h * a.os.sh) * ob;
+      const auto ro = rows_rsrc(opb + (int64_t)q0 * a.os.sn * ob, rows, ob * a.os.sn, ob * D);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int r = 32 * qb + ln;
+        float part = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint32_t off = (uint32_t)(r * ob * a.os.sn + ob * (16 * kc + 8 * g));
+          float o8[8];
+          if (a.o_f32) {
+            const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+            const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 16, 0, 0));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              o8[j] = lo[j];
+              o8[4 + j] = hi[j];
+            }
+          } else {
+            const bf16x8 v = buffer_load_bf16x8(ro, off);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o8[j] = (float)v[j];
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) part = fmaf((float)doreg[qb][kc][j], o8[j], part);
+        }
+        dsum[qb] = sum_halves(part);
+        if (split == 0 && g == 0 && r < rows) a.dsum[((int64_t)b * a.H + h) * a.Nq + q0 + r] = dsum[qb];
       }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) dsum[qb] = buffer_load_f32(rs, 4 * (32 * qb + ln));
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int r = 32 * qb + ln;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        qreg[qb][kc] = buffer_load_bf16x8(rq, (uint32_t)(r * 2 * a.qs.sn + 2 * (16 * kc + 8 * g)));
       const float l = buffer_load_f32(rl, 4 * r);
       lse2[qb] = r < rows ? l * kLog2e : INFINITY;
-      dsum[qb] = buffer_load_f32(rs, 4 * r);
     }
   }
 
@@ -1043,10 +1127,12 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int d, int in_bf16, hipStream_t s) {
   const long long grid = (rows + 15) / 16;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (in_bf16) {
+    const long long g2 = (2 * rows + 255) / 256;
+    if (g2 > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.o_f32)
-      hipLaunchKernelGGL((bwd_pre_kernel<bf16, float>), dim3((unsigned)grid), dim3(256), 0, s, a, d);
+      hipLaunchKernelGGL((bwd_pre_bf16_kernel<float>), dim3((unsigned)g2), dim3(256), 0, s, a, d);
     else
-      hipLaunchKernelGGL((bwd_pre_kernel<bf16, bf16>), dim3((unsigned)grid), dim3(256), 0, s, a, d);
+      hipLaunchKernelGGL((bwd_pre_bf16_kernel<bf16>), dim3((unsigned)g2), dim3(256), 0, s, a, d);
   } else {
     hipLaunchKernelGGL((bwd_pre_kernel<float, float>), dim3((unsigned)grid), dim3(256), 0, s, a, d);
   }
@@ -1132,12 +1218,13 @@ static hipError_t launch_dkdv_resident(const BwdArgs& a, hipStream_t s) {
 template <int D, int KW, int QW>
 static hipError_t bwd_bf16_d(const BwdArgs& a, int do_dkdv, int do_dq, int accumulate,
                              hipStream_t s) {
-  if (do_dkdv) {
-    const hipError_t e =
-        use_resident_dkdv(a) ? launch_dkdv_resident<D>(a, s) : launch_dkdv<D, KW>(a, s);
+  // dQ first: when it computes D (no preprocess), dK/dV reads that D
+  if (do_dq) {
+    const hipError_t e = launch_dq<D, QW>(a, accumulate, s);
     if (e != hipSuccess) return e;
   }
-  if (do_dq) return launch_dq<D, QW>(a, accumulate, s);
+  if (do_dkdv)
+    return use_resident_dkdv(a) ? launch_dkdv_resident<D>(a, s) : launch_dkdv<D, KW>(a, s);
   return hipSuccess;
 }
 
