@@ -261,6 +261,9 @@ def main():
     per_call = {c[0]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
                 for j, c in enumerate(calls)}
     ms = total_ms / K
+    step_ms = sorted(ev[i][0].elapsed_time(ev[i][n]) for i in range(K))
+    step_stats = {"median": round(float(np.median(step_ms)), 5), "min": round(step_ms[0], 5),
+                  "p90": round(float(np.percentile(step_ms, 90)), 5)}
 
     u = float(w.units)
     flops = 14.0 * u
@@ -303,6 +306,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "step_ms_stats": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -102,8 +102,12 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(BwdArgs a, int d) {
 // Query rows past Nq arrive as zeros with LSE = +inf (P = 0); key rows past
 // Nkv are zero and their gradients are never stored.
 // --------------------------------------------------------------------------
+// query rows per staged tile of the dK/dV kernel
+#ifndef EXATTN_DKDV_BM
+#define EXATTN_DKDV_BM 64
+#endif
 namespace bwdk {
-constexpr int BM = 64;
+constexpr int BM = EXATTN_DKDV_BM;
 constexpr int NT = 256;
 }  // namespace bwdk
 
@@ -362,11 +366,16 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     const uint32_t dbase = qbase + 2 * L::tile;
     tq.issue(rq, qbase, w);
     td.issue(rd, dbase, w);
+    // LSE then D, BM floats each, in 64-float wave instructions
     const uint32_t sbase = lds_address(stats + buf * 2 * BM);
-    if (w == 0)
-      buffer_load_lds4(rows_rsrc(lsep + q0, rows, 4, 4), sbase, 4 * lane);
-    else if (w == 1)
-      buffer_load_lds4(rows_rsrc(dsp + q0, rows, 4, 4), sbase + 4 * BM, 4 * lane);
+    constexpr int NSI = BM / 64;
+#pragma unroll
+    for (int c = w; c < 2 * NSI; c += 4) {
+      const int part = c % NSI;
+      const float* src = c < NSI ? lsep : dsp;
+      buffer_load_lds4(rows_rsrc(src + q0, rows, 4, 4),
+                       sbase + (c < NSI ? 0 : 4 * BM) + 256 * part, 256 * part + 4 * lane);
+    }
   };
 
   f32x16 dk[NCB][NDB], dv[NCB][NDB];

@@ -86,10 +86,13 @@ def test_tiny_f32_workload():
     _say(f"tiny_f32 errors {errs}")
 
 
-def test_strided_views():
-    """Q as a head-strided slice and K/V as views into wider buffers."""
-    g = np.random.Generator(np.random.PCG64(77))
-    B, H, Nq, Nkv, d = 2, 3, 150, 260, 64
+@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 3, 150, 260, 64), (1, 2, 40, 1100, 64),
+                                         (1, 2, 100, 700, 128)])
+def test_strided_views(B, H, Nq, Nkv, d):
+    """Q as a head-strided slice and K/V as views into wider buffers; the
+    short-query cases take the resident-query dK/dV kernel and the split dQ."""
+    _say(f"strided {B}x{H}x{Nq}x{Nkv}x{d}")
+    g = np.random.Generator(np.random.PCG64(77 + Nkv))
     big = synth.round_to_bf16(g.standard_normal((B, H + 2, Nq + 10, d), dtype=np.float32))
     kv = synth.round_to_bf16(g.standard_normal((B, H, Nkv + 40, 2 * d), dtype=np.float32))
     do = synth.round_to_bf16(g.standard_normal((B, H, Nq, d), dtype=np.float32))
@@ -99,7 +102,7 @@ def test_strided_views():
     v = kvd[:, :, 8:Nkv + 8, d:]
     x = {"q": big[:, 1:H + 1, 5:Nq + 5], "k": kv[:, :, 8:Nkv + 8, :d],
          "v": kv[:, :, 8:Nkv + 8, d:], "do": do}
-    scale = 0.125
+    scale = float(np.float32(1 / np.sqrt(d)))
     o, lse = ebw.fwd(q, k, v, scale=scale)
     dq, dk, dv = ebw.bwd(q, k, v, o, to_dev(do, "bf16"), lse, scale=scale)
     torch.cuda.synchronize()
@@ -111,14 +114,26 @@ def test_strided_views():
 
 def test_fp32_output_of_bf16_inputs():
     x = synth.random_case(5, 1, 2, 100, 300, 128, "bf16")
-    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    scale = float(np.float32(128 ** -0.5))
     o, lse = ebw.fwd(q, k, v, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], float(np.float32(128 ** -0.5)))
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], scale)
     assert o.dtype == torch.float32
     # fp32 output of bf16 products: no output rounding, so much tighter than 2e-2
     assert max_abs(to_host(o), o_ref) < 4e-3
     assert max_abs(to_host(lse), lse_ref) < 1e-3
+    # the backward from an fp32 O: D formed in the dQ kernel and by the
+    # preprocess kernel give the same bits
+    full = ebw.bwd(q, k, v, o, do, lse)
+    ws = torch.empty(ebw.bwd_workspace_bytes(q, k) // 4, dtype=torch.float32, device="cuda")
+    ebw.bwd_preprocess(o, do, ws)
+    split = ebw.bwd(q, k, v, None, do, lse, workspace=ws, d_precomputed=True)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(full, split):
+        assert torch.equal(a_, b_)
+    check_grads([to_host(t) for t in full], oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale),
+                "bf16", "fp32 O")
 
 
 @pytest.mark.parametrize("n_chunks,Nkv,d", [(8, 1000, 128), (3, 500, 64), (8, 5, 64), (4, 4096, 80)])
