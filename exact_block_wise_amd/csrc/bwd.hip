@@ -121,17 +121,18 @@ struct DkdvLds {
 };
 
 // One 32-query block against a wave's NCB x 32 keys: S = Q K^T and
-// dP = dO V^T (queries as A operands, the wave's K / V rows as B operands),
-// P = exp2(S log2e scale - LSE2), dS = P (dP - D), then dV += P^T dO and
-// dK += dS^T Q with the accumulator halves as A operands and the dO / Q
-// columns from LDS transpose reads.  Qs / dOs: row-major bf16 query rows
-// (row stride rs), lse2s / Ds: their LSE in log2 units (natural log with
-// LSE_NATURAL) and D.
-template <int D, int NCB, bool PIN, bool LSE_NATURAL = false>
+// E = D - dP (queries as A operands, the wave's K rows and NEGATED V rows as
+// B operands, the matrix-core chain of E starting from D instead of zero),
+// P = exp2(S log2e scale - LSE2), -dS = P E, then dV += P^T dO and
+// (-dK) += (-dS)^T Q with the accumulator halves as A operands and the dO / Q
+// columns from LDS transpose reads.  Folding D into the accumulator and the
+// sign into V leaves one multiply per score for dS.  Qs / dOs: row-major bf16
+// query rows (row stride rs), lse2s / Ds: their LSE in log2 units and D.
+template <int D, int NCB, bool PIN>
 __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int rs,
                                             const float* lse2s, const float* Ds, int nb,
                                             float sl2, const bf16x8 (&kreg)[NCB][D / 16],
-                                            const bf16x8 (&vreg)[NCB][D / 16],
+                                            const bf16x8 (&vneg)[NCB][D / 16],
                                             f32x16 (&dk)[NCB][(D + 31) / 32],
                                             f32x16 (&dv)[NCB][(D + 31) / 32], int lane) {
   constexpr int KC = D / 16, NDB = (D + 31) / 32;
@@ -142,38 +143,43 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
     qa[kc] = load_bf16x8(&Qs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
     da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
   }
-  f32x16 s[NCB], dp[NCB];
+  // D of the accumulator rows: entry 4i + r is query 32nb + 8i + 4g + r
+  f32x16 dinit;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[32 * nb + 8 * i + 4 * g]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dinit[4 * i + r] = d4[r];
+  }
+  f32x16 s[NCB], e[NCB];
   prio_mfma();
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     s[cb] = f32x16{};
-    dp[cb] = f32x16{};
+    e[cb] = dinit;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       s[cb] = mfma32(qa[kc], kreg[cb][kc], s[cb]);
-      dp[cb] = mfma32(da[kc], vreg[cb][kc], dp[cb]);
+      e[cb] = mfma32(da[kc], vneg[cb][kc], e[cb]);
     }
   }
   prio_valu();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int qi = 32 * nb + 8 * i + 4 * g;
-    f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[qi]);
-    if constexpr (LSE_NATURAL) l4 *= kLog2e;  // staged as stored (natural log)
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[qi]);
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * nb + 8 * i + 4 * g]);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = fast_exp2(fmaf(s[cb][4 * i + r], sl2, -l4[r]));
         s[cb][4 * i + r] = p;
-        dp[cb][4 * i + r] = p * (dp[cb][4 * i + r] - d4[r]);
+        e[cb][4 * i + r] *= p;
       }
   }
-  // dV^T += dO^T P, dK^T += Q^T dS over two 16-query chunks t = 2 nb + hh:
-  // slot group g holds queries 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3).
-  // The dO / Q columns (LDS transpose reads) are the A operands and the
-  // accumulator halves of P and dS the B operands, so the gradients come
+  // dV^T += dO^T P, (-dK)^T += Q^T (-dS) over two 16-query chunks t = 2 nb +
+  // hh: slot group g holds queries 16t + 4g + (0..3) and 16t + 8 + 4g +
+  // (0..3).  The dO / Q columns (LDS transpose reads) are the A operands and
+  // the accumulator halves of P and -dS the B operands, so the gradients come
   // out transposed: a lane owns one key and runs of 4 consecutive d, which
   // leave in 8-byte stores.
   prio_mfma();
@@ -184,7 +190,7 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       pa[cb] = acc_half_to_bf16(s[cb], hh);
-      sa[cb] = acc_half_to_bf16(dp[cb], hh);
+      sa[cb] = acc_half_to_bf16(e[cb], hh);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -205,16 +211,30 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
   prio_valu();
 }
 
-// dK (scaled) and dV of a wave's keys kw .. kw + 32 NCB - 1 from the
-// transposed accumulators: lane owns key kw + 32cb + ln and, per 32-column
-// block db, the runs d = 32db + 8i + 4g + (0..3) (accumulator entries
-// 4i .. 4i+3), each written as one 8-byte store.
+// V rows as the negated B operands dkdv_qblock takes (sign bits flipped)
+template <int NCB, int KC>
+__device__ __forceinline__ void negate_rows(bf16x8 (&v)[NCB][KC]) {
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 u = __builtin_bit_cast(u32x4, v[cb][kc]);
+      u ^= 0x80008000u;
+      v[cb][kc] = __builtin_bit_cast(bf16x8, u);
+    }
+}
+
+// dK and dV of a wave's keys kw .. kw + 32 NCB - 1 from the transposed
+// accumulators (dk holds -dK / scale, see dkdv_qblock): lane owns key
+// kw + 32cb + ln and, per 32-column block db, the runs d = 32db + 8i + 4g +
+// (0..3) (accumulator entries 4i .. 4i+3), each written as one 8-byte store.
 template <int D, int NCB>
 __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, int kw,
                                            const f32x16 (&dk)[NCB][(D + 31) / 32],
                                            const f32x16 (&dv)[NCB][(D + 31) / 32], int lane) {
   constexpr int NDB = (D + 31) / 32;
   const int ln = lane & 31, g = lane >> 5;
+  const float ks = -a.scale;
   bf16* dkp = (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh;
   bf16* dvp = (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh;
 #pragma unroll
@@ -229,8 +249,8 @@ __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, int k
         if (d0 >= D) continue;
         const f32x16& k16 = dk[cb][db];
         const f32x16& v16 = dv[cb][db];
-        const bf16x4 k4 = {(bf16)(k16[4 * i] * a.scale), (bf16)(k16[4 * i + 1] * a.scale),
-                           (bf16)(k16[4 * i + 2] * a.scale), (bf16)(k16[4 * i + 3] * a.scale)};
+        const bf16x4 k4 = {(bf16)(k16[4 * i] * ks), (bf16)(k16[4 * i + 1] * ks),
+                           (bf16)(k16[4 * i + 2] * ks), (bf16)(k16[4 * i + 3] * ks)};
         const bf16x4 v4 = {(bf16)v16[4 * i], (bf16)v16[4 * i + 1], (bf16)v16[4 * i + 2],
                            (bf16)v16[4 * i + 3]};
         *reinterpret_cast<bf16x4*>(dkp + (int64_t)kr * a.dks.sn + d0) = k4;
@@ -238,18 +258,6 @@ __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, int k
       }
   }
 }
-
-// stage query tiles with direct-to-LDS loads instead of through registers
-#ifndef EXATTN_DKDV_DMA
-#define EXATTN_DKDV_DMA 1
-#endif
-// query tiles in flight per workgroup: a second register set (2) fits at
-// d = 64 only at the edge of spilling and measured no faster there
-#ifndef EXATTN_DKDV_PF2
-#define EXATTN_DKDV_PF2 0
-#endif
-template <int D, int KW>
-constexpr int dkdv_prefetch() { return EXATTN_DKDV_PF2 && D <= 64 && KW == 32 ? 2 : 1; }
 
 template <int D, int KW>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
@@ -261,8 +269,6 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   // registers fit without spilling (see mfma32_agpr)
   constexpr bool kPinAcc = EXATTN_PIN_ACC && (KW == 64 || D > 80);
   constexpr int BN = 4 * KW;                   // key rows per workgroup
-  constexpr int CH = BM * (D / 8);             // 16-byte pieces per Q (or dO) tile
-  constexpr int PT = (CH + NT - 1) / NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16* const lds = reinterpret_cast<bf16*>(smem);
   float* const stats = reinterpret_cast<float*>(lds + L::n_bf16);  // [2][LSE2 | D][BM]
@@ -304,61 +310,19 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       }
   }
 
-  // Query tile loader: unconditional buffer loads (rows past Nq come back as
-  // zeros; their LSE is then set to +inf so that P = 0), so no branch sits
-  // between a load and the wait before its LDS store.
-  uint32_t qoff[PT], doff[PT];
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = tid + u * NT;
-    const int r = e / (D / 8), cc = e % (D / 8);
-    qoff[u] = (uint32_t)(r * 2 * a.qs.sn + 16 * cc);
-    doff[u] = (uint32_t)(r * 2 * a.dos.sn + 16 * cc);
-  }
-  constexpr int PF = dkdv_prefetch<D, KW>();
-  bf16x8 pq[2][PT], pd[2][PT];
-  float pst[2] = {0.f, 0.f};
-  auto load_tile = [&](auto set_tag, int q0) {
-    constexpr int S = decltype(set_tag)::value;
-    const int rows = a.Nq - q0;
-    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
-    const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      pq[S][u] = buffer_load_bf16x8(rq, qoff[u]);
-      pd[S][u] = buffer_load_bf16x8(rd, doff[u]);
-    }
-    // threads 0 .. BM-1: LSE (log2 units) of query q0 + tid; BM .. 2BM-1: D
-    const int r = tid & (BM - 1);
-    const float l = buffer_load_f32(rows_rsrc(lsep + q0, rows, 4, 4), 4 * r);
-    const float dd = buffer_load_f32(rows_rsrc(dsp + q0, rows, 4, 4), 4 * r);
-    pst[S] = tid < BM ? (r < rows ? l * kLog2e : INFINITY) : dd;
-  };
-  auto store_tile = [&](auto set_tag, int buf) {
-    constexpr int S = decltype(set_tag)::value;
-    bf16* Qs = lds + buf * 2 * L::tile;
-    bf16* dOs = Qs + L::tile;
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int e = tid + u * NT;
-      if (CH % NT == 0 || e < CH) {
-        const int r = e / (D / 8), cc = e % (D / 8);
-        *reinterpret_cast<bf16x8*>(&Qs[r * RS + 8 * cc]) = pq[S][u];
-        *reinterpret_cast<bf16x8*>(&dOs[r * RS + 8 * cc]) = pd[S][u];
-      }
-    }
-    if (tid < 2 * BM) stats[buf * 2 * BM + tid] = pst[S];
-  };
-
-  // Direct-to-LDS staging of the query tiles (no registers, no LDS stores
-  // in the loop; see LdsTileDma).  LSE and D are staged as stored
-  // (natural-log LSE); query rows past Nq read as zero, and with Q = dO = 0
-  // and D = 0 their P is finite and their dS and dO rows are zero, so they
-  // add nothing.
+  // Query tiles are staged with direct-to-LDS loads (no registers, no LDS
+  // stores in the loop; see LdsTileDma), and so is D.  The LSE goes through
+  // registers of the first BM / 64 waves, which convert it to log2 units once
+  // per staged row (instead of once per score) when the tile lands.  Query
+  // rows past Nq read as zero (Q = dO = 0, LSE = D = 0): their P is finite
+  // and their dS and dO rows are zero, so they add nothing.
+  constexpr int NSI = BM / 64;                 // 64-float pieces of LSE (and of D)
+  static_assert(NSI >= 1 && 2 * NSI <= 4, "one statistics piece per wave");
   LdsTileDma<D, RS, BM> tq, td;
   tq.init(w, lane, a.qs.sn);
   td.init(w, lane, a.dos.sn);
-  auto load_tile_dma = [&](int q0, int buf) {
+  float lse_next = 0.f;
+  auto load_tile = [&](int q0, int buf) {
     const int rows = a.Nq - q0;
     const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
     const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
@@ -366,16 +330,17 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     const uint32_t dbase = qbase + 2 * L::tile;
     tq.issue(rq, qbase, w);
     td.issue(rd, dbase, w);
-    // LSE then D, BM floats each, in 64-float wave instructions
-    const uint32_t sbase = lds_address(stats + buf * 2 * BM);
-    constexpr int NSI = BM / 64;
-#pragma unroll
-    for (int c = w; c < 2 * NSI; c += 4) {
-      const int part = c % NSI;
-      const float* src = c < NSI ? lsep : dsp;
-      buffer_load_lds4(rows_rsrc(src + q0, rows, 4, 4),
-                       sbase + (c < NSI ? 0 : 4 * BM) + 256 * part, 256 * part + 4 * lane);
+    if (w < NSI) {
+      lse_next = buffer_load_f32(rows_rsrc(lsep + q0, rows, 4, 4), 4 * (64 * w + lane));
+    } else if (w < 2 * NSI) {
+      const int part = w - NSI;
+      buffer_load_lds4(rows_rsrc(dsp + q0, rows, 4, 4),
+                       lds_address(stats + buf * 2 * BM + BM + 64 * part), 256 * part + 4 * lane);
     }
+  };
+  // after the tile's loads have landed (wait_vmem), before the barrier
+  auto finish_tile = [&](int buf) {
+    if (w < NSI) stats[buf * 2 * BM + 64 * w + lane] = lse_next * kLog2e;
   };
 
   f32x16 dk[NCB][NDB], dv[NCB][NDB];
@@ -389,78 +354,35 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const float sl2 = a.scale * kLog2e;
   const int nqt = (a.Nq + BM - 1) / BM;
 
-  // One query tile; NEXT: tile it + 1 exists (its loads are issued before
-  // and stored after this tile's work, without a run-time test).
-  auto tile = [&](auto tail_tag, auto set_tag, int it) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    constexpr int SET = decltype(set_tag)::value;
-    using LoadSet = std::integral_constant<int, PF == 2 ? SET : 0>;
-    using StoreSet = std::integral_constant<int, PF == 2 ? 1 - SET : 0>;
-    const int buf = PF == 2 ? SET : (it & 1);
-    if (!TAIL || it + PF < nqt) load_tile(LoadSet{}, (it + PF) * BM);
+  // one query tile; NEXT: tile it + 1 exists and is staged into the other
+  // buffer while this one is computed (waited for before the barrier)
+  auto tile = [&](auto next_tag, int it) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const int buf = it & 1;
+    if (NEXT) load_tile((it + 1) * BM, buf ^ 1);
     if (wave_active) {
       const bf16* Qs = lds + buf * 2 * L::tile;
       const bf16* dOs = Qs + L::tile;
       const float* lse2s = stats + buf * 2 * BM;
       const float* Ds = lse2s + BM;
       // one 32-row query block at a time keeps the live registers of a block
-      // (its S, dP and operands) from being doubled by interleaving
+      // (its S, E and operands) from being doubled by interleaving
 #pragma unroll 1
       for (int nb = 0; nb < BM / 32; ++nb)
         dkdv_qblock<D, NCB, kPinAcc>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
     }
-    if (!TAIL || it + 1 < nqt) store_tile(StoreSet{}, buf ^ 1);
+    wait_vmem();
+    if (NEXT) finish_tile(buf ^ 1);
     __syncthreads();
   };
-  if constexpr (EXATTN_DKDV_DMA) {
-    // one query tile; NEXT: tile it + 1 exists and is staged into the other
-    // buffer while this one is computed (waited for before the barrier)
-    auto tile_dma = [&](auto next_tag, int it) {
-      constexpr bool NEXT = decltype(next_tag)::value;
-      const int buf = it & 1;
-      if (NEXT) load_tile_dma((it + 1) * BM, buf ^ 1);
-      if (wave_active) {
-        const bf16* Qs = lds + buf * 2 * L::tile;
-        const bf16* dOs = Qs + L::tile;
-        const float* lses = stats + buf * 2 * BM;
-        const float* Ds = lses + BM;
-#pragma unroll 1
-        for (int nb = 0; nb < BM / 32; ++nb)
-          dkdv_qblock<D, NCB, kPinAcc, true>(Qs, dOs, RS, lses, Ds, nb, sl2, kreg, vreg, dk, dv,
-                                             lane);
-      }
-      wait_vmem();
-      __syncthreads();
-    };
-    load_tile_dma(0, 0);
-    wait_vmem();
-    __syncthreads();
-    int it = 0;
-    for (; it + 1 < nqt; ++it) tile_dma(std::true_type{}, it);
-    tile_dma(std::false_type{}, it);
-  } else {
-  using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    load_tile(S0{}, 0);
-    store_tile(S0{}, 0);
-    if (PF == 2 && nqt > 1) load_tile(S1{}, BM);
-    __syncthreads();
-    int it = 0;
-    if constexpr (PF == 2) {
-      for (; it + 3 < nqt; it += 2) {
-        tile(std::false_type{}, S0{}, it);
-        tile(std::false_type{}, S1{}, it + 1);
-      }
-      for (; it < nqt; it += 2) {
-        tile(std::true_type{}, S0{}, it);
-        if (it + 1 < nqt) tile(std::true_type{}, S1{}, it + 1);
-      }
-    } else {
-      for (; it + 1 < nqt; ++it) tile(std::false_type{}, S0{}, it);
-      tile(std::true_type{}, S0{}, it);
-    }
-  
-  }
+  load_tile(0, 0);
+  wait_vmem();
+  finish_tile(0);
+  negate_rows(vreg);  // landed with the wait above
+  __syncthreads();
+  int it = 0;
+  for (; it + 1 < nqt; ++it) tile(std::true_type{}, it);
+  tile(std::false_type{}, it);
 
   if (!wave_active) return;
   if constexpr (kPinAcc) agpr_results_ready();
@@ -571,6 +493,7 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
   bf16x8 kreg[1][KC], vreg[1][KC], knext[1][KC], vnext[1][KC];
   f32x16 dk[1][NDB], dv[1][NDB];
   auto block = [&](int kb_) {
+    negate_rows(vreg);
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
       dk[0][i] = f32x16{};
@@ -732,6 +655,19 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       lse2[qb] = r < rows ? l * kLog2e : INFINITY;
     }
   }
+  // E^T = D - dP^T: the matrix-core chain of dP^T = V dO^T runs on the
+  // negated dO rows and starts from D (every entry of a lane's accumulator
+  // belongs to its query), so dS needs one multiply per score: -dS = P E.
+  // At d = 80 the 16 registers of D do not fit three waves per SIMD; there
+  // D is added per score instead.
+  constexpr bool kFoldD = D != 80;
+  f32x16 dinit[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dinit[qb][e] = kFoldD ? dsum[qb] : 0.f;
+  }
+  negate_rows(doreg);
 
   const int n_kv = min(a.Nkv - kv_lo, a.dq_split_len);
   const int ntiles = (n_kv + BN - 1) / BN;
@@ -829,7 +765,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           st[cb][qb] = f32x16{};
-          dpt[cb][qb] = f32x16{};
+          dpt[cb][qb] = dinit[qb];
         }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -848,9 +784,9 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const float p = fast_exp2(fmaf(st[cb][qb][e], sl2, -lse2[qb]));
-            st[cb][qb][e] = p * (dpt[cb][qb][e] - dsum[qb]);
+            st[cb][qb][e] = p * (kFoldD ? dpt[cb][qb][e] : dpt[cb][qb][e] + dsum[qb]);
           }
-      // dQ += dS K over four 16-key chunks (slot group g: keys 16t + 4g +
+      // -dQ += (-dS) K over four 16-key chunks (slot group g: keys 16t + 4g +
       // (0..3) and 16t + 8 + 4g + (0..3) = accumulator entries 8hh..8hh+7)
       prio_mfma();
 #pragma unroll
@@ -910,7 +846,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       for (int e = 0; e < 16; ++e) {
         const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
         if (qr >= a.Nq) continue;
-        const float v = dq[qb][db][e] * a.scale;
+        const float v = dq[qb][db][e] * -a.scale;
         if (a.dq_splits > 1) {  // this key range's share, summed by dq_reduce_kernel
           a.dq_part[((((int64_t)split * a.B + b) * a.H + h) * a.Nq + qr) * D + dcol] = v;
         } else if (accumulate) {
