@@ -54,14 +54,21 @@ def parse():
 # HBM traffic of the dominant kernel, from hardware counters
 # --------------------------------------------------------------------------
 KERNEL_SOURCES = {"fwd": "fwd.hip", "fwd_chunked": "fwd.hip", "bwd_dkdv": "bwd.hip",
-                  "bwd_dq": "bwd.hip"}
+                  "bwd_dq": "bwd.hip", "bwd": "short.hip"}
 KERNEL_SYMBOLS = {"fwd": "fwd_", "fwd_chunked": "fwd_", "bwd_dkdv": "dkdv_",
-                  "bwd_dq": "dq_bf16_kernel"}
+                  "bwd_dq": "dq_bf16_kernel", "bwd": "bwd_short_kernel"}
 COPY_BYTES = 1 << 31  # 2 GiB read and 2 GiB written by the calibration copy
 
 
-def source_digest(call):
-    path = os.path.join(ROOT, "exact_block_wise_amd", "csrc", KERNEL_SOURCES[call])
+def is_short(w):
+    """Short sequences (both sides <= 32 rows, bf16): served by the
+    packed-tile kernels, whose backward is one call."""
+    return w.dtype == "bf16" and w.chunks == 1 and w.Nq <= 32 and w.Nkv <= 32
+
+
+def source_digest(call, short=False):
+    src = "short.hip" if short else KERNEL_SOURCES[call]
+    path = os.path.join(ROOT, "exact_block_wise_amd", "csrc", src)
     h = hashlib.sha256()
     for p in (path, os.path.join(ROOT, "exact_block_wise_amd", "csrc", "common.hpp")):
         h.update(open(p, "rb").read())
@@ -96,6 +103,8 @@ def _pmc_per_dispatch(d, counter, name_part):
 
 
 def make_traffic_profile(dirs, workload):
+    from exact_block_wise_amd import synth
+    short = is_short(synth.WORKLOADS[workload])
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
     cf = _pmc_per_dispatch(cfetch_dir, "FETCH_SIZE", "copy") * 1024 / COPY_BYTES
     cw = _pmc_per_dispatch(cwrite_dir, "WRITE_SIZE", "copy") * 1024 / COPY_BYTES
@@ -107,7 +116,8 @@ def make_traffic_profile(dirs, workload):
         except SystemExit:
             continue
         traffic = fk * 1024 / cf + wk * 1024 / cw
-        lines.append(f"{call} source={source_digest(call)} fetch_kib={fk:.1f} write_kib={wk:.1f} "
+        lines.append(f"{call} source={source_digest(call, short)} fetch_kib={fk:.1f} "
+                     f"write_kib={wk:.1f} "
                      f"traffic_bytes={traffic:.0f}")
     out = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
     with open(out, "w") as f:
@@ -131,7 +141,7 @@ def make_traffic_profile(dirs, workload):
     print(open(out).read())
 
 
-def measured_traffic(call, workload):
+def measured_traffic(call, workload, short=False):
     """traffic_bytes of `call` from profiles/, or None if absent or stale."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
@@ -139,7 +149,7 @@ def measured_traffic(call, workload):
     for ln in open(path):
         if ln.startswith(call + " "):
             kv = dict(x.split("=", 1) for x in ln.split()[1:])
-            if kv.get("source") == source_digest(call):
+            if kv.get("source") == source_digest(call, short):
                 return int(float(kv["traffic_bytes"]))
     return None
 
@@ -236,11 +246,18 @@ def main():
     else:
         calls.append(("fwd", 4.0, 4.0,
                       lambda: ebw.fwd(q, k, v, scale=w.scale, out=o, lse=lse)))
-    calls.append(("bwd_dq", 2.0, 6.0, lambda: ebw.bwd(
-        q, k, v, o, do, lse, scale=w.scale, dq=dq, workspace=ws, need_dkdv=False)))
-    calls.append(("bwd_dkdv", 8.0, 8.0, lambda: ebw.bwd(
-        q, k, v, None, do, lse, scale=w.scale, dk=dk, dv=dv, workspace=ws,
-        d_precomputed=True, need_dq=False)))
+    short = is_short(w)
+    if short:
+        # one backward call (the packed-tile kernel forms D, dQ, dK and dV in
+        # one pass; its seven products are 14 units, 10 credited)
+        calls.append(("bwd", 10.0, 14.0, lambda: ebw.bwd(
+            q, k, v, o, do, lse, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)))
+    else:
+        calls.append(("bwd_dq", 2.0, 6.0, lambda: ebw.bwd(
+            q, k, v, o, do, lse, scale=w.scale, dq=dq, workspace=ws, need_dkdv=False)))
+        calls.append(("bwd_dkdv", 8.0, 8.0, lambda: ebw.bwd(
+            q, k, v, None, do, lse, scale=w.scale, dk=dk, dv=dv, workspace=ws,
+            d_precomputed=True, need_dq=False)))
 
     for _ in range(args.warmup):
         for c in calls:
@@ -271,6 +288,21 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     fwd_ms = sum(per_call[c[0]] for c in calls if c[0] in ("fwd", "fwd_chunked", "lse_merge"))
     bwd_ms = ms - fwd_ms
+    # Algorithmic bytes of each call (compulsory HBM traffic: every input read
+    # once, every output written once; partials, re-reads and padding are
+    # overhead).  The roofline that bounds the dominant call follows from its
+    # arithmetic intensity against the ridge point peak / HBM bandwidth.
+    bpe = 2 if w.dtype == "bf16" else 4
+    kv_bytes = 2 * w.B * w.H * w.Nkv * w.d * bpe     # K and V (or dK and dV)
+    q_bytes = w.B * w.H * w.Nq * w.d * bpe           # one query-side tensor
+    row_bytes = w.B * w.H * w.Nq * 4                  # one fp32 per query row
+    alg_table = {
+        "fwd": kv_bytes + 2 * q_bytes + row_bytes,                     # Q,K,V -> O, LSE
+        "fwd_chunked": kv_bytes + q_bytes,                             # Q, K, V read
+        "bwd_dq": kv_bytes + 4 * q_bytes + 2 * row_bytes,              # Q,K,V,dO,O,LSE -> dQ, D
+        "bwd_dkdv": 2 * kv_bytes + 2 * q_bytes + 2 * row_bytes,        # Q,K,V,dO,LSE,D -> dK,dV
+        "bwd": 2 * kv_bytes + 4 * q_bytes + 2 * row_bytes,             # ... -> dQ, dK, dV, D
+    }
     kernels = {}
     for name, credit, executed, _ in calls:
         t = per_call[name]
@@ -278,25 +310,26 @@ def main():
         if credit:
             kernels[name]["tflops"] = round(credit * u / (t * 1e-3) / 1e12, 3)
             kernels[name]["executed_tflops"] = round(executed * u / (t * 1e-3) / 1e12, 3)
+            kernels[name]["algorithmic_gbs"] = round(alg_table[name] / (t * 1e-3) / 1e9, 1)
     dom = max((c for c in calls if c[1] > 0), key=lambda c: per_call[c[0]])
     dom_t = per_call[dom[0]]
-    if w.chunks > 1:
-        # long-KV cross-attention: HBM-bound; algorithmic bytes of the kernel
-        bpe = 2
-        kv_bytes = 2 * w.B * w.H * w.Nkv * w.d * bpe
-        q_bytes = w.B * w.H * w.Nq * w.d * bpe
-        alg = {"fwd_chunked": kv_bytes + q_bytes,
-               "bwd_dkdv": 2 * kv_bytes + 2 * q_bytes + 2 * w.B * w.H * w.Nq * 4,
-               "bwd_dq": 2 * q_bytes + q_bytes + 2 * w.B * w.H * w.Nq * 4}[dom[0]]
-        achieved = alg / (dom_t * 1e-3) / 1e9
+    alg_bytes = alg_table[dom[0]]
+    intensity = dom[1] * u / alg_bytes
+    if intensity < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = alg_bytes / (dom_t * 1e-3) / 1e9
         roof = {"kernel": dom[0], "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic(dom[0], w.name)}
+                "traffic": measured_traffic(dom[0], w.name, short),
+                "algorithmic_bytes": alg_bytes, "flop_per_byte": round(intensity, 1)}
     else:
+        # bf16 products run on the matrix cores; the fp32 path is plain
+        # vector FMAs (bound "alu", against the published fp32 vector peak)
         achieved = dom[1] * u / (dom_t * 1e-3) / 1e12
-        roof = {"kernel": dom[0], "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+        roof = {"kernel": dom[0], "bound": "mfma" if w.dtype == "bf16" else "alu",
+                "achieved": round(achieved, 3), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(dom[0], w.name)}
+                "traffic": measured_traffic(dom[0], w.name, short),
+                "algorithmic_bytes": alg_bytes, "flop_per_byte": round(intensity, 1)}
 
     line = {
         "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, video ViT-B N=1568",

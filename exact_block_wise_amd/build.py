@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libexattn.so")
-SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "merge.hip"]
+SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "merge.hip", "short.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -1175,6 +1175,8 @@ static hipError_t bwd_bf16_d(const BwdArgs& a, int do_dkdv, int do_dq, int accum
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
                            hipStream_t s) {
+  if (EXATTN_SHORT && short_slot(a.Nq, a.Nkv))
+    return launch_bwd_short(a, d, do_dkdv, do_dq, accumulate, s);
   switch (d) {
     case 64: return bwd_bf16_d<64, 32, 32>(a, do_dkdv, do_dq, accumulate, s);
     case 80: return bwd_bf16_d<80, 32, 32>(a, do_dkdv, do_dq, accumulate, s);

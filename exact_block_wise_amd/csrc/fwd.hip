@@ -1113,6 +1113,7 @@ static hipError_t fwd_bf16_d(const FwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t s) {
+  if (EXATTN_SHORT && a.n_chunks == 1 && short_slot(a.Nq, a.Nkv)) return launch_fwd_short(a, d, s);
   switch (d) {
     case 64: return fwd_bf16_d<64, EXATTN_FWD_QW64>(a, s);
     case 80: return fwd_bf16_d<80, EXATTN_FWD_QW80>(a, s);

@@ -67,6 +67,18 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int d, int do_dkdv, int do_dq, int a
                           hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
+// Short sequences (bf16, Nq and Nkv <= 32): several sequences per product
+// tile (EXATTN_SHORT=0 sends them through the general kernels instead).
+// short_slot is the rows per sequence in a tile (8, 16 or 32), or 0 when the
+// problem is not short.
+#ifndef EXATTN_SHORT
+#define EXATTN_SHORT 1
+#endif
+int short_slot(int Nq, int Nkv);
+hipError_t launch_fwd_short(const FwdArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_short(const BwdArgs& a, int d, int do_dkdv, int do_dq, int accumulate,
+                            hipStream_t s);
+
 // Number of key ranges the bf16 dQ pass splits Nkv into (1 = unsplit): a
 // split is used only when the query blocks alone would leave most compute
 // units idle (a short query block against a long key range).

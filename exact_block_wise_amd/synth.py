@@ -60,6 +60,13 @@ WORKLOADS = {
     "vit_h14": Workload(4, "vit_h14", 8, 16, 2048, 2048, 80, "bf16"),
     # 128 text tokens against 256 frames x 128 visual tokens, 8 KV chunks
     "xattn": Workload(5, "xattn", 4, 32, 128, 32768, 128, "bf16", chunks=8),
+    # The ViT-B clips above (32 clips, 8 x 14 x 14 tubelet grid, 12 heads,
+    # d = 64) under divided space-time attention: temporal attention over the
+    # 8 time steps of each of the 32 * 196 spatial positions, and spatial
+    # attention over the 196 positions of each of the 32 * 8 time steps
+    # (sequences flattened into the batch axis).
+    "vit_b_temporal": Workload(6, "vit_b_temporal", 32 * 196, 12, 8, 8, 64, "bf16"),
+    "vit_b_spatial": Workload(7, "vit_b_spatial", 32 * 8, 12, 196, 196, 64, "bf16"),
 }
 
 
