@@ -366,9 +366,11 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       const float* lse2s = stats + buf * 2 * BM;
       const float* Ds = lse2s + BM;
       // one 32-row query block at a time keeps the live registers of a block
-      // (its S, E and operands) from being doubled by interleaving
+      // (its S, E and operands) from being doubled by interleaving; blocks
+      // wholly past Nq (in the last tile) are skipped
+      const int nbs = min(BM / 32, (a.Nq - it * BM + 31) / 32);
 #pragma unroll 1
-      for (int nb = 0; nb < BM / 32; ++nb)
+      for (int nb = 0; nb < nbs; ++nb)
         dkdv_qblock<D, NCB, kPinAcc>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
     }
     wait_vmem();
@@ -536,15 +538,6 @@ constexpr int BN = 64;
 constexpr int NT = 256;
 }  // namespace dqk
 
-// stage key/value tiles with direct-to-LDS loads instead of through registers
-#ifndef EXATTN_DQ_DMA
-#define EXATTN_DQ_DMA 1
-#endif
-// key/value tiles in flight per workgroup (a second register set, 2, fits
-// at d = 64 but measured no faster there)
-template <int D>
-constexpr int dq_prefetch() { return 1; }
-
 template <int D>
 struct DqLds {
   static constexpr int DP = (D + 31) / 32 * 32;
@@ -560,8 +553,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   constexpr int DP = L::DP, NDB = DP / 32, KC = D / 16, KS = L::KS;
   constexpr int NQB = QW / 32;
   constexpr int BM = 4 * QW;
-  constexpr int CH = BN * (D / 8);
-  constexpr int PT = (CH + NT - 1) / NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16* const lds = reinterpret_cast<bf16*>(smem);
 
@@ -671,46 +662,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
 
   const int n_kv = min(a.Nkv - kv_lo, a.dq_split_len);
   const int ntiles = (n_kv + BN - 1) / BN;
-  // key/value tile loader: unconditional buffer loads, rows past Nkv zero
-  uint32_t koff[PT], voff[PT];
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = tid + u * NT;
-    const int r = e / (D / 8), cc = e % (D / 8);
-    koff[u] = (uint32_t)(r * 2 * a.ks.sn + 16 * cc);
-    voff[u] = (uint32_t)(r * 2 * a.vs.sn + 16 * cc);
-  }
-  // two register sets where they fit: tile t is loaded into set t % 2 two
-  // tiles ahead and stored to LDS buffer t % 2 one tile ahead
-  constexpr int PF = dq_prefetch<D>();
-  bf16x8 pk[2][PT], pv[2][PT];
-  auto load_tile = [&](auto set_tag, int j0) {
-    constexpr int S = decltype(set_tag)::value;
-    const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
-    const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      pk[S][u] = buffer_load_bf16x8(rk, koff[u]);
-      pv[S][u] = buffer_load_bf16x8(rv, voff[u]);
-    }
-  };
-  auto store_tile = [&](auto set_tag, int buf) {
-    constexpr int S = decltype(set_tag)::value;
-    bf16* Kt = lds + buf * 2 * L::tile;
-    bf16* Vt = Kt + L::tile;
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int e = tid + u * NT;
-      if (CH % NT == 0 || e < CH) {
-        const int r = e / (D / 8), cc = e % (D / 8);
-        *reinterpret_cast<bf16x8*>(&Kt[r * KS + 8 * cc]) = pk[S][u];
-        *reinterpret_cast<bf16x8*>(&Vt[r * KS + 8 * cc]) = pv[S][u];
-      }
-    }
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-
   f32x16 dq[NQB][NDB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb)
@@ -718,11 +669,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     for (int db = 0; db < NDB; ++db) dq[qb][db] = f32x16{};
   const float sl2 = a.scale * kLog2e;
 
-  // direct-to-LDS staging of the key/value tiles (see LdsTileDma)
+  // direct-to-LDS staging of the key/value tiles (see LdsTileDma); rows
+  // past the end of the key range read as zeros
   LdsTileDma<D, KS, BN> tk, tv;
   tk.init(w, lane, a.ks.sn);
   tv.init(w, lane, a.vs.sn);
-  auto load_tile_dma = [&](int j0, int buf) {
+  auto load_tile = [&](int j0, int buf) {
     const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
     const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
     const uint32_t kbase = lds_address(lds + buf * 2 * L::tile);
@@ -730,22 +682,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     tv.issue(rv, kbase + 2 * L::tile, w);
   };
 
-  // One key/value tile.  In the steady state (TAIL false) tile it + PF is
-  // loaded and tile it + 1 stored without a run-time test; the last tiles
-  // test both.  With PF = 2 the register set SET = it % 2 receives tile
-  // it + 2 and LDS buffer SET is read; with PF = 1 one set is used and the
-  // buffer alternates at run time.
-  auto tile = [&](auto tail_tag, auto set_tag, int it) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    constexpr int SET = decltype(set_tag)::value;
-    using LoadSet = std::integral_constant<int, PF == 2 ? SET : 0>;
-    using StoreSet = std::integral_constant<int, PF == 2 ? 1 - SET : 0>;
-    const int buf = PF == 2 ? SET : (it & 1);
-    if constexpr (EXATTN_DQ_DMA) {
-      if (!TAIL || it + 1 < ntiles) load_tile_dma((it + 1) * BN, buf ^ 1);
-    } else {
-      if (!TAIL || it + PF < ntiles) load_tile(LoadSet{}, (it + PF) * BN);
-    }
+  // One key/value tile; NEXT: tile it + 1 exists and is staged into the
+  // other buffer while this one is computed (waited for before the barrier).
+  auto tile = [&](auto next_tag, int it) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const int buf = it & 1;
+    if (NEXT) load_tile((it + 1) * BN, buf ^ 1);
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
@@ -803,36 +745,15 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       }
       prio_valu();
     }
-    if constexpr (EXATTN_DQ_DMA) {
-      wait_vmem();
-    } else {
-      if (!TAIL || it + 1 < ntiles) store_tile(StoreSet{}, buf ^ 1);
-    }
+    wait_vmem();
     __syncthreads();
   };
-  if constexpr (EXATTN_DQ_DMA) {
-    load_tile_dma(0, 0);
-    wait_vmem();
-  } else {
-    load_tile(S0{}, 0);
-    store_tile(S0{}, 0);
-    if (PF == 2 && ntiles > 1) load_tile(S1{}, BN);
-  }
+  load_tile(0, 0);
+  wait_vmem();
   __syncthreads();
   int it = 0;
-  if constexpr (PF == 2 && !EXATTN_DQ_DMA) {
-    for (; it + 3 < ntiles; it += 2) {
-      tile(std::false_type{}, S0{}, it);
-      tile(std::false_type{}, S1{}, it + 1);
-    }
-    for (; it < ntiles; it += 2) {
-      tile(std::true_type{}, S0{}, it);
-      if (it + 1 < ntiles) tile(std::true_type{}, S1{}, it + 1);
-    }
-  } else {
-    for (; it + 1 < ntiles; ++it) tile(std::false_type{}, S0{}, it);
-    tile(std::true_type{}, S0{}, it);
-  }
+  for (; it + 1 < ntiles; ++it) tile(std::true_type{}, it);
+  tile(std::false_type{}, it);
 
   if (!wave_active) return;
   // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block
