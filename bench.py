@@ -60,10 +60,23 @@ KERNEL_SYMBOLS = {"fwd": "fwd_", "fwd_chunked": "fwd_", "bwd_dkdv": "dkdv_",
 COPY_BYTES = 1 << 31  # 2 GiB read and 2 GiB written by the calibration copy
 
 
+def is_packed(w):
+    """Variable-length sequences packed along one token axis."""
+    return hasattr(w, "lens")
+
+
 def is_short(w):
     """Short sequences (both sides <= 32 rows, bf16): served by the
     packed-tile kernels, whose backward is one call."""
-    return w.dtype == "bf16" and w.chunks == 1 and w.Nq <= 32 and w.Nkv <= 32
+    return (not is_packed(w) and w.dtype == "bf16" and w.chunks == 1 and w.Nq <= 32
+            and w.Nkv <= 32)
+
+
+def find_workload(name):
+    from exact_block_wise_amd import synth
+    if name in synth.PACKED_WORKLOADS:
+        return synth.PACKED_WORKLOADS[name]
+    return synth.WORKLOADS[name]
 
 
 def source_digest(call, short=False):
@@ -103,8 +116,7 @@ def _pmc_per_dispatch(d, counter, name_part):
 
 
 def make_traffic_profile(dirs, workload):
-    from exact_block_wise_amd import synth
-    short = is_short(synth.WORKLOADS[workload])
+    short = is_short(find_workload(workload))
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
     cf = _pmc_per_dispatch(cfetch_dir, "FETCH_SIZE", "copy") * 1024 / COPY_BYTES
     cw = _pmc_per_dispatch(cwrite_dir, "WRITE_SIZE", "copy") * 1024 / COPY_BYTES
@@ -157,6 +169,13 @@ def measured_traffic(call, workload, short=False):
 def upload(w, torch):
     from exact_block_wise_amd import synth
     dev = {}
+    if is_packed(w):
+        for n in ("q", "k", "v", "do"):
+            host = synth.packed_tensor(w, n)
+            dev[n] = torch.from_numpy(synth.bf16_bits(host)).view(torch.bfloat16).cuda()
+            del host
+        dev["cu"] = torch.from_numpy(w.cu).cuda()
+        return dev
     for n in ("q", "k", "v", "do"):
         nrows = w.Nq if n in ("q", "do") else w.Nkv
         host = synth.full_tensor(w.cid, n, w.B, w.H, nrows, w.d, w.dtype)
@@ -178,12 +197,21 @@ def cpu_baseline(w, budget_s):
         threads = max([i["num_threads"] for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
-    heads, t_work = 0, 0.0
-    per_head = 14.0 * w.Nq * w.Nkv * w.d
-    order = [(b, h) for b in range(w.B) for h in range(w.H)]
+    heads, t_work, flops = 0, 0.0, 0.0
+    if is_packed(w):
+        order = [(s_, h) for s_ in range(len(w.lens)) for h in range(w.H)]
+    else:
+        order = [(b, h) for b in range(w.B) for h in range(w.H)]
     while t_work < budget_s and heads < len(order):
         b, h = order[heads]
-        x = synth.workload_head(w, b, h)
+        if is_packed(w):
+            n = w.lens[b]
+            x = {t: synth.head_tensor(w.cid, t, b, h, w.H, n, w.d, w.dtype)
+                 for t in ("q", "k", "v", "do")}
+            flops += 14.0 * n * n * w.d
+        else:
+            x = synth.workload_head(w, b, h)
+            flops += 14.0 * w.Nq * w.Nkv * w.d
         t0 = time.perf_counter()
         if w.chunks > 1:
             L = w.Nkv // w.chunks
@@ -196,10 +224,10 @@ def cpu_baseline(w, budget_s):
             oracle.head_bwd(x["q"], x["k"], x["v"], x["do"], w.scale)
         t_work += time.perf_counter() - t0
         heads += 1
-    return {"value": round(per_head * heads / t_work / 1e12, 6), "unit": "TFLOP/s",
+    return {"value": round(flops / t_work / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads (b,h) of {w.name}, fwd+bwd in fp64 "
-                      f"NumPy, {t_work:.1f} s"}
+            "sample": f"{heads} of {len(order)} heads (sequence, head) of {w.name}, fwd+bwd in "
+                      f"fp64 NumPy, {t_work:.1f} s"}
 
 
 def main():
@@ -218,14 +246,21 @@ def main():
     import exact_block_wise_amd as ebw
     from exact_block_wise_amd import synth
 
-    w = synth.WORKLOADS[args.workload]
+    w = find_workload(args.workload)
+    packed = is_packed(w)
     dev = upload(w, torch)
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     tdt = q.dtype
-    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=tdt, device="cuda")
-    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(ebw.bwd_workspace_bytes(q, k) // 4, dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    if packed:
+        cu, mx = dev["cu"], max(w.lens)
+        lse = torch.empty((w.H, w.tokens), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ebw.bwd_varlen_workspace_bytes(q, k, cu, cu, mx, mx) // 4,
+                         dtype=torch.float32, device="cuda")
+    else:
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ebw.bwd_workspace_bytes(q, k) // 4, dtype=torch.float32, device="cuda")
     if w.chunks > 1:
         o_parts = torch.empty((w.chunks, w.B, w.H, w.Nq, w.d), dtype=torch.float32, device="cuda")
         lse_parts = torch.empty((w.chunks, w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
@@ -238,7 +273,17 @@ def main():
     # workspace, which the dK/dV call then reads (the fp32 path runs the
     # preprocess inside the dQ call instead).
     calls = []
-    if w.chunks > 1:
+    short = is_short(w)
+    if packed:
+        calls.append(("fwd", 4.0, 4.0, lambda: ebw.fwd_varlen(
+            q, k, v, cu, cu, mx, mx, scale=w.scale, out=o, lse=lse)))
+        calls.append(("bwd_dq", 2.0, 6.0, lambda: ebw.bwd_varlen(
+            q, k, v, o, do, lse, cu, cu, mx, mx, scale=w.scale, dq=dq, workspace=ws,
+            need_dkdv=False)))
+        calls.append(("bwd_dkdv", 8.0, 8.0, lambda: ebw.bwd_varlen(
+            q, k, v, None, do, lse, cu, cu, mx, mx, scale=w.scale, dk=dk, dv=dv, workspace=ws,
+            d_precomputed=True, need_dq=False)))
+    elif w.chunks > 1:
         calls.append(("fwd_chunked", 4.0, 4.0, lambda: ebw.fwd_chunked(
             q, k, v, w.chunks, scale=w.scale, o_parts=o_parts, lse_parts=lse_parts)))
         calls.append(("lse_merge", 0.0, 0.0,
@@ -246,8 +291,9 @@ def main():
     else:
         calls.append(("fwd", 4.0, 4.0,
                       lambda: ebw.fwd(q, k, v, scale=w.scale, out=o, lse=lse)))
-    short = is_short(w)
-    if short:
+    if packed:
+        pass
+    elif short:
         # one backward call (the packed-tile kernel forms D, dQ, dK and dV in
         # one pass; its seven products are 14 units, 10 credited)
         calls.append(("bwd", 10.0, 14.0, lambda: ebw.bwd(
@@ -293,9 +339,11 @@ def main():
     # overhead).  The roofline that bounds the dominant call follows from its
     # arithmetic intensity against the ridge point peak / HBM bandwidth.
     bpe = 2 if w.dtype == "bf16" else 4
-    kv_bytes = 2 * w.B * w.H * w.Nkv * w.d * bpe     # K and V (or dK and dV)
-    q_bytes = w.B * w.H * w.Nq * w.d * bpe           # one query-side tensor
-    row_bytes = w.B * w.H * w.Nq * 4                  # one fp32 per query row
+    q_rows = w.tokens * w.H if packed else w.B * w.H * w.Nq      # query rows (all heads)
+    kv_rows = w.tokens * w.H if packed else w.B * w.H * w.Nkv
+    kv_bytes = 2 * kv_rows * w.d * bpe               # K and V (or dK and dV)
+    q_bytes = q_rows * w.d * bpe                     # one query-side tensor
+    row_bytes = q_rows * 4                           # one fp32 per query row
     alg_table = {
         "fwd": kv_bytes + 2 * q_bytes + row_bytes,                     # Q,K,V -> O, LSE
         "fwd_chunked": kv_bytes + q_bytes,                             # Q, K, V read
@@ -345,8 +393,12 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. N(0,1) per head, rounded to the compute dtype",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
-                   "kv_chunks": w.chunks, "scale": w.scale},
+        "config": ({"workload": w.name, "H": w.H, "d": w.d, "sequences": len(w.lens),
+                    "tokens": w.tokens, "lengths": "x".join(map(str, sorted(set(w.lens)))) +
+                    f" (each x{len(w.lens) // len(set(w.lens))})", "scale": w.scale}
+                   if packed else
+                   {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "d": w.d,
+                    "kv_chunks": w.chunks, "scale": w.scale}),
         "pct_of_peak": round(100.0 * value / peak, 2),
         "fwd_ms": round(fwd_ms, 5),
         "bwd_ms": round(bwd_ms, 5),

@@ -10,6 +10,8 @@ or fails to load, every call raises.
     dq, dk, dv = bwd(q, k, v, o, do, lse)
     o_parts, lse_parts = fwd_chunked(q, k, v, n_chunks=8)
     o, lse = lse_merge(o_parts, lse_parts)
+    o, lse = fwd_varlen(q, k, v, cu_q, cu_kv, max_q, max_kv)   # packed [T,H,d]
+    dq, dk, dv = bwd_varlen(q, k, v, o, do, lse, cu_q, cu_kv, max_q, max_kv)
 """
 from __future__ import annotations
 
@@ -20,7 +22,8 @@ import os
 import torch  # imported first so the library binds to torch's HIP runtime
 
 __all__ = ["fwd", "fwd_chunked", "lse_merge", "bwd", "bwd_preprocess",
-           "bwd_workspace_bytes", "ExattnError", "library_path", "load", "ABI_VERSION",
+           "bwd_workspace_bytes", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
+           "ExattnError", "library_path", "load", "ABI_VERSION",
            "BWD_DQ_ACCUMULATE", "BWD_D_PRECOMPUTED", "BWD_NO_DQ", "BWD_NO_DKDV"]
 
 ABI_VERSION = 1
@@ -48,6 +51,13 @@ class _Tensor(ctypes.Structure):
 class _Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
                 ("Nkv", ctypes.c_int32), ("d", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _Varlen(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("max_q", ctypes.c_int32), ("max_kv", ctypes.c_int32),
+                ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("cu_q", ctypes.c_void_p), ("cu_kv", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,6 +95,13 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_preprocess.argtypes = [P, T, T, fp, vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [P, T, T, T, T, T, fp, T, T, T, vp, sz, u32, vp]
+    V = ctypes.POINTER(_Varlen)
+    lib.attn_fwd_varlen.restype = ctypes.c_int
+    lib.attn_fwd_varlen.argtypes = [V, T, T, T, T, fp, vp]
+    lib.attn_bwd_varlen_workspace_bytes.restype = sz
+    lib.attn_bwd_varlen_workspace_bytes.argtypes = [V]
+    lib.attn_bwd_varlen.restype = ctypes.c_int
+    lib.attn_bwd_varlen.argtypes = [V, T, T, T, T, T, fp, T, T, T, vp, sz, u32, vp]
     if lib.attn_abi_version() != ABI_VERSION:
         raise ExattnError("load", -1, f"ABI version {lib.attn_abi_version()} != {ABI_VERSION}")
     _lib = lib
@@ -237,4 +254,94 @@ def bwd(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
                         _desc_or_null(dk if need_dkdv else None),
                         _desc_or_null(dv if need_dkdv else None),
                         workspace.data_ptr(), ws_bytes, flags, _stream(q.device)))
+    return (dq if need_dq else None, dk if need_dkdv else None, dv if need_dkdv else None)
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length sequences: q, o, dout [Tq, H, d]; k, v [Tkv, H, d];
+# cu_q / cu_kv int32 prefix sums on the GPU; lse [H, Tq].
+# --------------------------------------------------------------------------
+
+def _packed_desc(t: torch.Tensor) -> _Tensor:
+    if t.dim() != 3:
+        raise ValueError(f"expected a packed [T,H,d] tensor, got shape {tuple(t.shape)}")
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return _Tensor(t.data_ptr(), _DTYPES[t.dtype], 0, t.stride(1), t.stride(0))
+
+
+def _packed_desc_or_null(t):
+    return _packed_desc(t) if t is not None else _Tensor(None, _BF16, 0, 0, 0)
+
+
+def _varlen(q, k, cu_q, cu_kv, max_q, max_kv, scale) -> _Varlen:
+    for name, c in (("cu_q", cu_q), ("cu_kv", cu_kv)):
+        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous() or c.dim() != 1:
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if cu_q.numel() != cu_kv.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_q and cu_kv need n_seq + 1 >= 2 entries each")
+    Tq, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return _Varlen(cu_q.numel() - 1, H, d, int(max_q), int(max_kv), Tq, k.shape[0], scale,
+                   cu_q.data_ptr(), cu_kv.data_ptr())
+
+
+def fwd_varlen(q, k, v, cu_q, cu_kv, max_q, max_kv, scale=None, out=None, lse=None,
+               out_dtype=None):
+    """Forward over packed sequences.  Returns (o [Tq,H,d], lse [H,Tq] float32)."""
+    lib = load()
+    Tq, H, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, H, d), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    _check_f32_contig(lse, (H, Tq), "lse")
+    p = _varlen(q, k, cu_q, cu_kv, max_q, max_kv, scale)
+    _check("attn_fwd_varlen",
+           lib.attn_fwd_varlen(ctypes.byref(p), _packed_desc(q), _packed_desc(k),
+                               _packed_desc(v), _packed_desc(out), lse.data_ptr(),
+                               _stream(q.device)))
+    return out, lse
+
+
+def bwd_varlen_workspace_bytes(q, k, cu_q, cu_kv, max_q, max_kv) -> int:
+    p = _varlen(q, k, cu_q, cu_kv, max_q, max_kv, None)
+    return int(load().attn_bwd_varlen_workspace_bytes(ctypes.byref(p)))
+
+
+def bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_kv, max_q, max_kv, scale=None, dq=None,
+               dk=None, dv=None, accumulate_dq=False, workspace=None, d_precomputed=False,
+               need_dq=True, need_dkdv=True):
+    """Backward over packed sequences; arguments as bwd.  Returns (dq, dk, dv)."""
+    lib = load()
+    if need_dq and dq is None:
+        dq = (torch.zeros_like(q, dtype=torch.float32) if accumulate_dq else torch.empty_like(q))
+    if need_dkdv and dk is None:
+        dk = torch.empty_like(k)
+    if need_dkdv and dv is None:
+        dv = torch.empty_like(v)
+    Tq, H, d = q.shape
+    _check_f32_contig(lse, (H, Tq), "lse")
+    flags = ((BWD_DQ_ACCUMULATE if accumulate_dq else 0) |
+             (BWD_D_PRECOMPUTED if d_precomputed else 0) |
+             (0 if need_dq else BWD_NO_DQ) | (0 if need_dkdv else BWD_NO_DKDV))
+    p = _varlen(q, k, cu_q, cu_kv, max_q, max_kv, scale)
+    need = lib.attn_bwd_varlen_workspace_bytes(ctypes.byref(p))
+    if workspace is None:
+        if d_precomputed:
+            raise ValueError("d_precomputed needs the workspace that holds D")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("attn_bwd_varlen",
+           lib.attn_bwd_varlen(ctypes.byref(p), _packed_desc(q), _packed_desc(k),
+                               _packed_desc(v), _packed_desc_or_null(o), _packed_desc(dout),
+                               lse.data_ptr(), _packed_desc_or_null(dq if need_dq else None),
+                               _packed_desc_or_null(dk if need_dkdv else None),
+                               _packed_desc_or_null(dv if need_dkdv else None),
+                               workspace.data_ptr(), ws_bytes, flags, _stream(q.device)))
     return (dq if need_dq else None, dk if need_dkdv else None, dv if need_dkdv else None)

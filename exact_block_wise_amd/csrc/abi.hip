@@ -71,6 +71,26 @@ bool pre_dtypes_ok(int o_dtype, int do_dtype) {
                                : o_dtype == ATTN_F32;
 }
 
+attn_status check_varlen(const attn_varlen* p) {
+  if (!p) return ATTN_E_INVALID;
+  if (p->n_seq < 1 || p->H < 1 || p->d < 1 || p->max_q < 1 || p->max_kv < 1) return ATTN_E_INVALID;
+  if (p->total_q < 0 || p->total_kv < 0 || !p->cu_q || !p->cu_kv) return ATTN_E_INVALID;
+  if (!isfinite(p->scale)) return ATTN_E_INVALID;
+  if (!supported_d(p->d)) return ATTN_E_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(p->cu_q) % 4 || reinterpret_cast<uintptr_t>(p->cu_kv) % 4)
+    return ATTN_E_UNSUPPORTED;
+  // the statistics index h * total_q + t and the grid must fit their types
+  if ((int64_t)p->H * p->total_q > (int64_t(1) << 40)) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// packed tensors: token and head strides only
+Strides packed_strides(const attn_tensor& t) { return Strides{0, t.sh, t.sn}; }
+
+size_t varlen_dsum_bytes(const attn_varlen* p) {
+  return round_up((size_t)p->H * p->total_q * sizeof(float), kWsAlign);
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +250,99 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_t
     }
   }
   if (dt == ATTN_F32) return from_hip(launch_bwd_f32(a, p->d, do_dkdv, do_dq, acc, s));
+  return from_hip(launch_bwd_bf16(a, p->d, do_dkdv, do_dq, acc, s));
+}
+
+attn_status attn_fwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                            attn_tensor o, float* lse, void* stream) {
+  attn_status st = first_error({check_varlen(p), check_tensor(q), check_tensor(k),
+                                check_tensor(v), check_tensor(o)});
+  if (st != ATTN_OK) return st;
+  if (k.dtype != q.dtype || v.dtype != q.dtype) return ATTN_E_INVALID;
+  if (o.dtype != q.dtype && o.dtype != ATTN_F32) return ATTN_E_INVALID;
+  if (q.dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (!lse) return ATTN_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
+  FwdArgs a{};
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.o = o.ptr; a.lse = lse;
+  a.qs = packed_strides(q); a.ks = packed_strides(k); a.vs = packed_strides(v);
+  a.os = packed_strides(o);
+  a.B = p->n_seq; a.H = p->H; a.Nq = p->max_q; a.Nkv = p->max_kv;
+  a.n_chunks = 1; a.chunk_len = p->max_kv;
+  a.scale = p->scale;
+  a.out_f32 = o.dtype == ATTN_F32;
+  a.cu_q = p->cu_q; a.cu_kv = p->cu_kv; a.total_q = p->total_q;
+  return from_hip(launch_fwd_bf16(a, p->d, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_varlen_workspace_bytes(const attn_varlen* p) {
+  if (check_varlen(p) != ATTN_OK) return 0;
+  return varlen_dsum_bytes(p);
+}
+
+attn_status attn_bwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                            attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
+                            attn_tensor dk, attn_tensor dv, void* workspace,
+                            size_t workspace_bytes, uint32_t flags, void* stream) {
+  constexpr uint32_t kAll = ATTN_BWD_DQ_ACCUMULATE | ATTN_BWD_D_PRECOMPUTED | ATTN_BWD_NO_DQ |
+                            ATTN_BWD_NO_DKDV;
+  if (flags & ~kAll) return ATTN_E_INVALID;
+  const bool acc = flags & ATTN_BWD_DQ_ACCUMULATE;
+  const bool pre_done = flags & ATTN_BWD_D_PRECOMPUTED;
+  const bool do_dq = !(flags & ATTN_BWD_NO_DQ);
+  const bool do_dkdv = !(flags & ATTN_BWD_NO_DKDV);
+  if (!do_dq && !do_dkdv) return ATTN_E_INVALID;
+  attn_status st = first_error({check_varlen(p), check_tensor(q), check_tensor(k),
+                                check_tensor(v), check_tensor(dout),
+                                pre_done ? ATTN_OK : check_tensor(o),
+                                do_dq ? check_tensor(dq) : ATTN_OK,
+                                do_dkdv ? check_tensor(dk) : ATTN_OK,
+                                do_dkdv ? check_tensor(dv) : ATTN_OK});
+  if (st != ATTN_OK) return st;
+  const int dt = q.dtype;
+  if (k.dtype != dt || v.dtype != dt || dout.dtype != dt) return ATTN_E_INVALID;
+  if (dt != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (!pre_done && !pre_dtypes_ok(o.dtype, dt)) return ATTN_E_INVALID;
+  if (do_dkdv && (dk.dtype != dt || dv.dtype != dt)) return ATTN_E_INVALID;
+  if (do_dq && (acc ? dq.dtype != ATTN_F32 : dq.dtype != dt)) return ATTN_E_INVALID;
+  if (!lse) return ATTN_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
+  if (!workspace || workspace_bytes < varlen_dsum_bytes(p)) return ATTN_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return ATTN_E_WORKSPACE;
+
+  BwdArgs a{};
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.o = o.ptr; a.dout = dout.ptr; a.lse = lse;
+  a.dq = dq.ptr; a.dk = dk.ptr; a.dv = dv.ptr;
+  a.qs = packed_strides(q); a.ks = packed_strides(k); a.vs = packed_strides(v);
+  a.os = packed_strides(o); a.dos = packed_strides(dout); a.dqs = packed_strides(dq);
+  a.dks = packed_strides(dk); a.dvs = packed_strides(dv);
+  a.dsum = static_cast<float*>(workspace);
+  a.dq_part = nullptr;
+  a.dq_splits = 1;
+  a.dq_split_len = p->max_kv;
+  a.B = p->n_seq; a.H = p->H; a.Nq = p->max_q; a.Nkv = p->max_kv;
+  a.scale = p->scale;
+  a.o_f32 = o.dtype == ATTN_F32;
+  a.cu_q = p->cu_q; a.cu_kv = p->cu_kv; a.total_q = p->total_q;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!pre_done) {
+    if (do_dq) {
+      a.dq_computes_d = 1;  // the dQ kernel (or the packed-tile kernel) forms D
+    } else {
+      // D over all packed query tokens: the dense preprocess of one
+      // [1, H, total_q, d] problem writes the same [H, total_q] order
+      BwdArgs pa = a;
+      pa.cu_q = pa.cu_kv = nullptr;
+      pa.B = 1;
+      pa.Nq = (int)p->total_q;
+      pa.os.sb = pa.dos.sb = 0;
+      if (p->total_q > 0x7fffffffLL) return ATTN_E_UNSUPPORTED;
+      if (p->total_q > 0) {
+        const hipError_t e = launch_bwd_pre(pa, p->d, 1, s);
+        if (e != hipSuccess) return ATTN_E_HIP;
+      }
+    }
+  }
   return from_hip(launch_bwd_bf16(a, p->d, do_dkdv, do_dq, acc, s));
 }
 

@@ -229,18 +229,18 @@ __device__ __forceinline__ void negate_rows(bf16x8 (&v)[NCB][KC]) {
 // kw + 32cb + ln and, per 32-column block db, the runs d = 32db + 8i + 4g +
 // (0..3) (accumulator entries 4i .. 4i+3), each written as one 8-byte store.
 template <int D, int NCB>
-__device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, int kw,
-                                           const f32x16 (&dk)[NCB][(D + 31) / 32],
+__device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, const SeqSpan& sp,
+                                           int kw, const f32x16 (&dk)[NCB][(D + 31) / 32],
                                            const f32x16 (&dv)[NCB][(D + 31) / 32], int lane) {
   constexpr int NDB = (D + 31) / 32;
   const int ln = lane & 31, g = lane >> 5;
   const float ks = -a.scale;
-  bf16* dkp = (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh;
-  bf16* dvp = (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh;
+  bf16* dkp = (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh + (int64_t)sp.kv_row0 * a.dks.sn;
+  bf16* dvp = (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh + (int64_t)sp.kv_row0 * a.dvs.sn;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int kr = kw + 32 * cb + ln;
-    if (kr >= a.Nkv) continue;
+    if (kr >= sp.nkv) continue;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -283,23 +283,26 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   idx /= nkb;
   const int h = idx % a.H;
   const int b = idx / a.H;
+  const SeqSpan sp = seq_span(a, b, h);
+  if (kb * BN >= sp.nkv) return;  // a packed sequence shorter than the longest
 
-  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
-  const bf16* dop = (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh;
-  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh;
-  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh;
-  const float* lsep = a.lse + ((int64_t)b * a.H + h) * a.Nq;
-  const float* dsp = a.dsum + ((int64_t)b * a.H + h) * a.Nq;
+  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh + (int64_t)sp.q_row0 * a.qs.sn;
+  const bf16* dop =
+      (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh + (int64_t)sp.q_row0 * a.dos.sn;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh + (int64_t)sp.kv_row0 * a.ks.sn;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh + (int64_t)sp.kv_row0 * a.vs.sn;
+  const float* lsep = a.lse + sp.stat0;
+  const float* dsp = a.dsum + sp.stat0;
 
   const int kw = kb * BN + KW * w;             // first key row of this wave
-  const bool wave_active = kw < a.Nkv;
+  const bool wave_active = kw < sp.nkv;
 
   // this wave's K and V rows as B operands (lane: key kw + 32cb + ln,
   // d = 16kc + 8g .. +7; rows past Nkv read as zeros)
   bf16x8 kreg[NCB][KC], vreg[NCB][KC];
   {
-    const auto rk = rows_rsrc(kp + (int64_t)kw * a.ks.sn, a.Nkv - kw, 2 * a.ks.sn, 2 * D);
-    const auto rv = rows_rsrc(vp + (int64_t)kw * a.vs.sn, a.Nkv - kw, 2 * a.vs.sn, 2 * D);
+    const auto rk = rows_rsrc(kp + (int64_t)kw * a.ks.sn, sp.nkv - kw, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)kw * a.vs.sn, sp.nkv - kw, 2 * a.vs.sn, 2 * D);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -323,7 +326,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   td.init(w, lane, a.dos.sn);
   float lse_next = 0.f;
   auto load_tile = [&](int q0, int buf) {
-    const int rows = a.Nq - q0;
+    const int rows = sp.nq - q0;
     const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
     const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
     const uint32_t qbase = lds_address(lds + buf * 2 * L::tile);
@@ -352,7 +355,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       dv[cb][i] = f32x16{};
     }
   const float sl2 = a.scale * kLog2e;
-  const int nqt = (a.Nq + BM - 1) / BM;
+  const int nqt = max(1, (sp.nq + BM - 1) / BM);  // (no query rows: one empty tile)
 
   // one query tile; NEXT: tile it + 1 exists and is staged into the other
   // buffer while this one is computed (waited for before the barrier)
@@ -368,7 +371,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       // one 32-row query block at a time keeps the live registers of a block
       // (its S, E and operands) from being doubled by interleaving; blocks
       // wholly past Nq (in the last tile) are skipped
-      const int nbs = min(BM / 32, (a.Nq - it * BM + 31) / 32);
+      const int nbs = min(BM / 32, (sp.nq - it * BM + 31) / 32);
 #pragma unroll 1
       for (int nb = 0; nb < nbs; ++nb)
         dkdv_qblock<D, NCB, kPinAcc>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
@@ -388,7 +391,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 
   if (!wave_active) return;
   if constexpr (kPinAcc) agpr_results_ready();
-  dkdv_store<D, NCB>(a, b, h, kw, dk, dv, lane);
+  dkdv_store<D, NCB>(a, b, h, sp, kw, dk, dv, lane);
 }
 
 // --------------------------------------------------------------------------
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
     for (int nb = 0; nb < nqb; ++nb)
       dkdv_qblock<D, 1, kPin>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
     if constexpr (kPin) agpr_results_ready();
-    dkdv_store<D, 1>(a, b, h, kb_ * KB + 32 * w, dk, dv, lane);
+    dkdv_store<D, 1>(a, b, h, seq_span(a, b, h), kb_ * KB + 32 * w, dk, dv, lane);
   };
   load_kv(kb, kreg, vreg);
   for (; kb + groups < nkb; kb += groups) {
@@ -568,24 +571,29 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   idx /= a.dq_splits;
   const int h = idx % a.H;
   const int b = idx / a.H;
+  const SeqSpan sp = seq_span(a, b, h);
+  if (qblk * BM >= sp.nq) return;  // a packed sequence shorter than the longest
   const int kv_lo = split * a.dq_split_len;
 
-  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
-  const bf16* dop = (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh;
-  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh + (int64_t)kv_lo * a.ks.sn;
-  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh + (int64_t)kv_lo * a.vs.sn;
-  const float* lsep = a.lse + ((int64_t)b * a.H + h) * a.Nq;
-  const float* dsp = a.dsum + ((int64_t)b * a.H + h) * a.Nq;
+  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh + (int64_t)sp.q_row0 * a.qs.sn;
+  const bf16* dop =
+      (const bf16*)a.dout + b * a.dos.sb + h * a.dos.sh + (int64_t)sp.q_row0 * a.dos.sn;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh +
+                   (int64_t)(sp.kv_row0 + kv_lo) * a.ks.sn;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh +
+                   (int64_t)(sp.kv_row0 + kv_lo) * a.vs.sn;
+  const float* lsep = a.lse + sp.stat0;
+  const float* dsp = a.dsum + sp.stat0;
 
   const int q0 = qblk * BM + w * QW;
-  const bool wave_active = q0 < a.Nq;
+  const bool wave_active = q0 < sp.nq;
 
   // this wave's Q and dO rows as B operands, with their LSE (log2 units) and
   // D; rows past Nq read as zeros with LSE = +inf
   bf16x8 qreg[NQB][KC], doreg[NQB][KC];
   float lse2[NQB], dsum[NQB];
   {
-    const int rows = a.Nq - q0;
+    const int rows = sp.nq - q0;
     const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, rows, 2 * a.qs.sn, 2 * D);
     const auto rd = rows_rsrc(dop + (int64_t)q0 * a.dos.sn, rows, 2 * a.dos.sn, 2 * D);
     const auto rl = rows_rsrc(lsep + q0, rows, 4, 4);
@@ -603,7 +611,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       // lanes l and l + 32 hold the two halves of each row's d.  Key range 0
       // writes D for the dK/dV pass.
       const int ob = a.o_f32 ? 4 : 2;
-      const char* opb = (const char*)a.o + (b * a.os.sb + h * a.os.sh) * ob;
+      const char* opb =
+          (const char*)a.o + (b * a.os.sb + h * a.os.sh + (int64_t)sp.q_row0 * a.os.sn) * ob;
       const auto ro = rows_rsrc(opb + (int64_t)q0 * a.os.sn * ob, rows, ob * a.os.sn, ob * D);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
@@ -630,7 +639,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
           for (int j = 0; j < 8; ++j) part = fmaf((float)doreg[qb][kc][j], o8[j], part);
         }
         dsum[qb] = sum_halves(part);
-        if (split == 0 && g == 0 && r < rows) a.dsum[((int64_t)b * a.H + h) * a.Nq + q0 + r] = dsum[qb];
+        if (split == 0 && g == 0 && r < rows) a.dsum[sp.stat0 + q0 + r] = dsum[qb];
       }
     } else {
 #pragma unroll
@@ -660,7 +669,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   }
   negate_rows(doreg);
 
-  const int n_kv = min(a.Nkv - kv_lo, a.dq_split_len);
+  const int n_kv = min(sp.nkv - kv_lo, a.dq_split_len);
   const int ntiles = (n_kv + BN - 1) / BN;
   f32x16 dq[NQB][NDB];
 #pragma unroll
@@ -748,12 +757,15 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     wait_vmem();
     __syncthreads();
   };
-  load_tile(0, 0);
-  wait_vmem();
-  __syncthreads();
-  int it = 0;
-  for (; it + 1 < ntiles; ++it) tile(std::true_type{}, it);
-  tile(std::false_type{}, it);
+  // (a packed sequence without keys: dQ = 0)
+  if (n_kv > 0) {
+    load_tile(0, 0);
+    wait_vmem();
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < ntiles; ++it) tile(std::true_type{}, it);
+    tile(std::false_type{}, it);
+  }
 
   if (!wave_active) return;
   // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block
@@ -766,15 +778,17 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (qr >= a.Nq) continue;
+        if (qr >= sp.nq) continue;
         const float v = dq[qb][db][e] * -a.scale;
         if (a.dq_splits > 1) {  // this key range's share, summed by dq_reduce_kernel
           a.dq_part[((((int64_t)split * a.B + b) * a.H + h) * a.Nq + qr) * D + dcol] = v;
         } else if (accumulate) {
-          float* p = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)qr * a.dqs.sn + dcol;
+          float* p = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
+                     (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
           *p += v;
         } else {
-          bf16* p = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)qr * a.dqs.sn + dcol;
+          bf16* p = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
+                    (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
           *p = (bf16)v;
         }
       }
@@ -1062,7 +1076,8 @@ static int compute_units() {
 
 // resident query side: at most 128 query rows and at least 4 key blocks
 static bool use_resident_dkdv(const BwdArgs& a) {
-  return EXATTN_DKDV_RESIDENT && a.Nq <= resk::QR && (a.Nkv + resk::KB - 1) / resk::KB >= 4;
+  return EXATTN_DKDV_RESIDENT && !a.cu_q && a.Nq <= resk::QR &&
+         (a.Nkv + resk::KB - 1) / resk::KB >= 4;
 }
 
 template <int D>

@@ -78,23 +78,27 @@ void fwd_bf16_kernel(FwdArgs a) {
   idx /= a.H;
   const int b = idx % a.B;
   const int c = idx / a.B;
+  const SeqSpan sp = seq_span(a, b, h);
+  if (qblk * BM >= sp.nq) return;  // a packed sequence shorter than the longest
 
   const int kv_lo = c * a.chunk_len;
-  const int n_kv = max(0, min(a.Nkv, kv_lo + a.chunk_len) - kv_lo);
+  const int n_kv = max(0, min(sp.nkv, kv_lo + a.chunk_len) - kv_lo);
   const int ntiles = (n_kv + BN - 1) / BN;
 
-  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh;
-  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh + (int64_t)kv_lo * a.ks.sn;
-  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh + (int64_t)kv_lo * a.vs.sn;
+  const bf16* qp = (const bf16*)a.q + b * a.qs.sb + h * a.qs.sh + (int64_t)sp.q_row0 * a.qs.sn;
+  const bf16* kp = (const bf16*)a.k + b * a.ks.sb + h * a.ks.sh +
+                   (int64_t)(sp.kv_row0 + kv_lo) * a.ks.sn;
+  const bf16* vp = (const bf16*)a.v + b * a.vs.sb + h * a.vs.sh +
+                   (int64_t)(sp.kv_row0 + kv_lo) * a.vs.sn;
 
   const int q0 = qblk * BM + w * QW;
-  const bool wave_active = q0 < a.Nq;
+  const bool wave_active = q0 < sp.nq;
 
   // this wave's query rows as B operands: lane -> row q0 + 32 qb + ln,
   // d = 16 kc + 8 g .. +7 (rows past Nq read as zeros)
   bf16x8 qreg[NQB][KC];
   {
-    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, a.Nq - q0, 2 * a.qs.sn, 2 * D);
+    const auto rq = rows_rsrc(qp + (int64_t)q0 * a.qs.sn, sp.nq - q0, 2 * a.qs.sn, 2 * D);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -250,10 +254,10 @@ void fwd_bf16_kernel(FwdArgs a) {
   for (int qb = 0; qb < NQB; ++qb) {
     const float l = sum_halves(lsum[qb]);
     const int qrow = q0 + 32 * qb + ln;
-    if (qrow >= a.Nq) continue;
+    if (qrow >= sp.nq) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t orow = (int64_t)c * a.o_chunk_stride + b * a.os.sb + h * a.os.sh +
-                         (int64_t)qrow * a.os.sn;
+                         (int64_t)(sp.q_row0 + qrow) * a.os.sn;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -274,7 +278,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       }
     }
     if (g == 0) {
-      const int64_t li = (int64_t)c * a.lse_chunk_stride + ((int64_t)b * a.H + h) * a.Nq + qrow;
+      const int64_t li = (int64_t)c * a.lse_chunk_stride + sp.stat0 + qrow;
       a.lse[li] = l > 0.f ? (mref[qb] * sl2 + log2f(l)) * kLn2 : -INFINITY;
     }
   }

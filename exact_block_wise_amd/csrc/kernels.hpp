@@ -25,6 +25,13 @@ struct FwdArgs {
   int n_chunks, chunk_len;
   float scale;
   int out_f32;               // 1: o is fp32, 0: o is the input dtype
+  // Packed variable-length sequences (null: dense).  Sequence b owns query
+  // tokens [cu_q[b], cu_q[b+1]) and key/value tokens [cu_kv[b], cu_kv[b+1]);
+  // B is then the number of sequences, Nq / Nkv bound their lengths, sb is
+  // 0 (tokens are rows of stride sn) and LSE is [H, total_q].
+  const int* cu_q;
+  const int* cu_kv;
+  int64_t total_q;
 };
 
 struct BwdArgs {
@@ -46,7 +53,37 @@ struct BwdArgs {
   int dq_splits;     // key ranges the dQ pass is split into (1: none)
   int dq_split_len;  // keys per range, a multiple of the key tile
   int dq_computes_d; // the bf16 dQ kernel forms D from o and dout and writes dsum
+  // packed variable-length sequences, as in FwdArgs (LSE and D [H, total_q])
+  const int* cu_q;
+  const int* cu_kv;
+  int64_t total_q;
 };
+
+// The rows of one (sequence, head) problem: dense [B,H,N,d] tensors, or
+// packed variable-length sequences.
+struct SeqSpan {
+  int q_row0, kv_row0;  // first query / key token of the sequence (0: dense)
+  int nq, nkv;          // its query and key/value lengths
+  int64_t stat0;        // index of its first query row in LSE and D
+};
+template <typename Args>
+__device__ __forceinline__ SeqSpan seq_span(const Args& a, int b, int h) {
+  SeqSpan s;
+  if (a.cu_q) {
+    s.q_row0 = a.cu_q[b];
+    s.nq = a.cu_q[b + 1] - s.q_row0;
+    s.kv_row0 = a.cu_kv[b];
+    s.nkv = a.cu_kv[b + 1] - s.kv_row0;
+    s.stat0 = (int64_t)h * a.total_q + s.q_row0;
+  } else {
+    s.q_row0 = 0;
+    s.kv_row0 = 0;
+    s.nq = a.Nq;
+    s.nkv = a.Nkv;
+    s.stat0 = ((int64_t)b * a.H + h) * a.Nq;
+  }
+  return s;
+}
 
 struct MergeArgs {
   const float* o_parts;

@@ -28,16 +28,31 @@ namespace shortk {
 constexpr int ROWS = 32;  // rows of a wave's tile (query side and key side)
 }  // namespace shortk
 
-// Row r of a tile: sequence seq0 + r / S (a flat b*H + h index), slot r % S.
+// Row r of a tile belongs to problem x = seq0 + r / S (a flat b*H + h
+// index) at slot r % S.  A lane holds one row; Row describes it.
 template <int S>
-struct ShortTile {
-  int seq0, BH, H;
-  __device__ __forceinline__ bool seq_ok(int r) const { return seq0 + r / S < BH; }
-  __device__ __forceinline__ int64_t bh(int r) const { return (int64_t)seq0 + r / S; }
-  __device__ __forceinline__ int64_t off(const Strides& st, int r) const {
+struct ShortRow {
+  bool ok;     // the problem exists
+  int b, h, pos;
+  SeqSpan sp;  // its rows (dense, or a packed variable-length sequence)
+  template <typename Args>
+  __device__ __forceinline__ ShortRow(const Args& a, int seq0, int r) {
     const int x = seq0 + r / S;
-    return (int64_t)(x / H) * st.sb + (int64_t)(x % H) * st.sh + (int64_t)(r % S) * st.sn;
+    ok = x < a.B * a.H;
+    b = ok ? x / a.H : 0;
+    h = ok ? x % a.H : 0;
+    pos = r % S;
+    sp = seq_span(a, b, h);
   }
+  __device__ __forceinline__ bool q_ok() const { return ok && pos < sp.nq; }
+  __device__ __forceinline__ bool kv_ok() const { return ok && pos < sp.nkv; }
+  __device__ __forceinline__ int64_t q_off(const Strides& st) const {
+    return (int64_t)b * st.sb + (int64_t)h * st.sh + (int64_t)(sp.q_row0 + pos) * st.sn;
+  }
+  __device__ __forceinline__ int64_t kv_off(const Strides& st) const {
+    return (int64_t)b * st.sb + (int64_t)h * st.sh + (int64_t)(sp.kv_row0 + pos) * st.sn;
+  }
+  __device__ __forceinline__ int64_t stat() const { return sp.stat0 + pos; }
 };
 
 // One row per lane as matrix-core operands: lane (l % 32, g = l / 32) holds
@@ -83,14 +98,13 @@ void fwd_short_kernel(FwdArgs a) {
   constexpr int P = shortk::ROWS / S;
   __shared__ __attribute__((aligned(16))) bf16 vt[Dm::tile];
   const int lane = threadIdx.x, ln = lane & 31, g = lane >> 5;
-  const ShortTile<S> t{(int)blockIdx.x * P, a.B * a.H, a.H};
+  const ShortRow<S> row(a, (int)blockIdx.x * P, ln);  // this lane's query and key row
 
-  const bool rq = t.seq_ok(ln) && ln % S < a.Nq;   // this lane's query row exists
-  const bool rk = t.seq_ok(ln) && ln % S < a.Nkv;  // this lane's key row exists
+  const bool rq = row.q_ok(), rk = row.kv_ok();
   bf16x8 qb[KC], ka[KC], vr[KC];
-  load_row_operands(qb, (const bf16*)a.q + t.off(a.qs, ln), rq, g);
-  load_row_operands(ka, (const bf16*)a.k + t.off(a.ks, ln), rk, g);
-  load_row_operands(vr, (const bf16*)a.v + t.off(a.vs, ln), rk, g);
+  load_row_operands(qb, (const bf16*)a.q + row.q_off(a.qs), rq, g);
+  load_row_operands(ka, (const bf16*)a.k + row.kv_off(a.ks), rk, g);
+  load_row_operands(vr, (const bf16*)a.v + row.kv_off(a.vs), rk, g);
   stage_rows<KC, RS>(vt, vr, ln, g);
 
   f32x16 s = f32x16{};
@@ -103,13 +117,13 @@ void fwd_short_kernel(FwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int kr = 8 * (e >> 2) + 4 * g + (e & 3);
-    const bool ok = kr / S == c / S && kr % S < a.Nkv;
+    const bool ok = kr / S == c / S && kr % S < row.sp.nkv;
     s[e] = ok ? s[e] : -INFINITY;
     m = fmaxf(m, s[e]);
   }
   m = max_halves(m);
   const float sl2 = a.scale * kLog2e;
-  const float moff = m == -INFINITY ? 0.f : m * sl2;  // (a column with no keys: unused)
+  const float moff = m == -INFINITY ? 0.f : m * sl2;  // a query without keys: O = 0
   float l = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -133,8 +147,8 @@ void fwd_short_kernel(FwdArgs a) {
   }
 
   if (!rq) return;
-  const float inv = 1.f / l;  // l >= 1: the maximum's own weight is 1
-  const int64_t orow = t.off(a.os, c);
+  const float inv = l > 0.f ? 1.f / l : 0.f;  // l >= 1 when the query has keys
+  const int64_t orow = row.q_off(a.os);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -151,7 +165,7 @@ void fwd_short_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>((bf16*)a.o + orow + d0) = v4;
       }
     }
-  if (g == 0) a.lse[t.bh(c) * a.Nq + c % S] = m * a.scale + logf(l);
+  if (g == 0) a.lse[row.stat()] = l > 0.f ? m * a.scale + logf(l) : -INFINITY;
 }
 
 // --------------------------------------------------------------------------
@@ -184,24 +198,24 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
   float* const Dss = lse2s + shortk::ROWS;
 
   const int lane = threadIdx.x, ln = lane & 31, g = lane >> 5;
-  const ShortTile<S> t{(int)blockIdx.x * P, a.B * a.H, a.H};
-  const bool rq = t.seq_ok(ln) && ln % S < a.Nq;
-  const bool rk = t.seq_ok(ln) && ln % S < a.Nkv;
+  const ShortRow<S> row(a, (int)blockIdx.x * P, ln);  // this lane's query and key row
+  const bool rq = row.q_ok(), rk = row.kv_ok();
 
   bf16x8 qb[KC], ka[KC], va[KC], dob[KC];
-  load_row_operands(qb, (const bf16*)a.q + t.off(a.qs, ln), rq, g);
-  load_row_operands(ka, (const bf16*)a.k + t.off(a.ks, ln), rk, g);
-  load_row_operands(va, (const bf16*)a.v + t.off(a.vs, ln), rk, g);
-  load_row_operands(dob, (const bf16*)a.dout + t.off(a.dos, ln), rq, g);
+  load_row_operands(qb, (const bf16*)a.q + row.q_off(a.qs), rq, g);
+  load_row_operands(ka, (const bf16*)a.k + row.kv_off(a.ks), rk, g);
+  load_row_operands(va, (const bf16*)a.v + row.kv_off(a.vs), rk, g);
+  load_row_operands(dob, (const bf16*)a.dout + row.q_off(a.dos), rq, g);
 
-  // this lane's query row: LSE in log2 units (+inf for a missing row: P = 0)
-  // and D
-  const int64_t srow = t.bh(ln) * a.Nq + ln % S;
-  const float lse2 = rq ? a.lse[srow] * kLog2e : INFINITY;
+  // this lane's query row: LSE in log2 units and D.  A missing row, or one
+  // whose sequence has no keys (LSE = -inf), gets +inf: P = 0.
+  const int64_t srow = row.stat();
+  const float lse_r = rq ? a.lse[srow] : INFINITY;
+  const float lse2 = lse_r == -INFINITY ? INFINITY : lse_r * kLog2e;
   float dsum = 0.f;
   if (a.dq_computes_d) {
     const int ob = a.o_f32 ? 4 : 2;
-    const char* orow = (const char*)a.o + t.off(a.os, ln) * ob;
+    const char* orow = (const char*)a.o + row.q_off(a.os) * ob;
     float part = 0.f;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -251,7 +265,7 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int kr = 8 * (e >> 2) + 4 * g + (e & 3);
-      const bool ok = kr / S == c / S && kr % S < a.Nkv;
+      const bool ok = kr / S == c / S && kr % S < row.sp.nkv;
       const float p = ok ? fast_exp2(fmaf(s[e], sl2, -lse2)) : 0.f;
       s[e] = p * (dp[e] - dsum);
     }
@@ -268,7 +282,7 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
       }
     }
     if (rq) {
-      const int64_t qrow = t.off(a.dqs, c);
+      const int64_t qrow = row.q_off(a.dqs);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -333,7 +347,7 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
       }
     }
     if (rk) {
-      const int64_t krow = t.off(a.dks, c), vrow = t.off(a.dvs, c);
+      const int64_t krow = row.kv_off(a.dks), vrow = row.kv_off(a.dvs);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -70,6 +70,56 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class PackedWorkload:
+    """Variable-length sequences packed along one token axis ([T, H, d]),
+    each attending to itself.  Sequence s, head h draws its rows like head
+    (b = s, h) of a dense workload with the same cid."""
+    cid: int
+    name: str
+    H: int
+    d: int
+    lens: tuple       # tokens per sequence (queries = keys)
+    dtype: str = "bf16"
+    chunks: int = 1
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+    @property
+    def tokens(self) -> int:
+        return int(sum(self.lens))
+
+    @property
+    def units(self) -> int:
+        """sum over sequences of n*n*d, times H (the dense B*H*Nq*Nkv*d)."""
+        return self.H * self.d * int(sum(n * n for n in self.lens))
+
+    @property
+    def cu(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lens)]).astype(np.int32)
+
+
+PACKED_WORKLOADS = {
+    # Mixed image / video batch packed instead of padded (the sequence
+    # packing of the NeMo video-model page): ViT-B clips of 16, 8 and 4
+    # frames (8, 4, 2 tubelet steps of 14 x 14) and single images, eight of
+    # each, 12 heads, d = 64.
+    "vit_b_packed": PackedWorkload(8, "vit_b_packed", 12, 64, (1568, 784, 392, 196) * 8),
+}
+
+
+def packed_tensor(w: PackedWorkload, tensor: str) -> np.ndarray:
+    """The packed [T, H, d] tensor: sequence s, head h at rows cu[s]..cu[s+1]."""
+    cu = w.cu
+    out = np.empty((w.tokens, w.H, w.d), dtype=np.float32)
+    for s, n in enumerate(w.lens):
+        for h in range(w.H):
+            out[cu[s]:cu[s + 1], h] = head_tensor(w.cid, tensor, s, h, w.H, n, w.d, w.dtype)
+    return out
+
+
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bfloat16 (ties to even); returns fp32."""
     x = np.ascontiguousarray(x, dtype=np.float32)

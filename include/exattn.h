@@ -209,6 +209,58 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k,
                      attn_tensor dv, void* workspace, size_t workspace_bytes,
                      uint32_t flags, void* stream);
 
+/*
+ * Packed variable-length sequences ("THD" layout).
+ *
+ * n_seq sequences of different lengths concatenated along one token axis,
+ * the sequence packing of mixed image / video batches (NeMo video-model
+ * page, "Efficient multimodal dataloading": variable-length images and
+ * videos packed up to a maximum sequence length instead of padded).  Each
+ * sequence attends only to itself: its query tokens [cu_q[s], cu_q[s+1])
+ * against its key/value tokens [cu_kv[s], cu_kv[s+1]), with the same
+ * softmax, LSE and gradients as a separate attn_fwd / attn_bwd per sequence.
+ *
+ *   q, o, dout, dq: [total_q, H, d]; k, v, dk, dv: [total_kv, H, d], as
+ *      attn_tensor with sb ignored: token t, head h at t*sn + h*sh.
+ *   lse (and D in the workspace): [H, total_q] fp32 contiguous.
+ *   cu_q, cu_kv: DEVICE int32 arrays of n_seq + 1 prefix sums, non-
+ *      decreasing, cu[0] = 0, cu_q[n_seq] = total_q, cu_kv[n_seq] =
+ *      total_kv.  A sequence may be empty on either side (no keys: O = 0,
+ *      LSE = -inf, dQ = 0; no queries: dK = dV = 0).
+ *   max_q, max_kv: host bounds (>= 1) on every sequence's query and key
+ *      lengths; they size the launch.  The arrays are not read on the host:
+ *      arrays that break these rules (a length above its bound, sums out of
+ *      order or past the tensors) make the kernels address rows outside the
+ *      tensors, so the caller must guarantee them.
+ * BF16 only (F32 is ATTN_E_UNSUPPORTED); d in {64, 80, 128}.  Sequences with
+ * both lengths <= 32 take the packed-tile kernels, longer ones the general
+ * kernels (the resident-query dK/dV and split-key dQ variants are not used).
+ */
+typedef struct {
+  int32_t n_seq, H, d;
+  int32_t max_q, max_kv;
+  int64_t total_q, total_kv;
+  float scale;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+} attn_varlen;
+
+attn_status attn_fwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                            attn_tensor o, float* lse, void* stream);
+
+/* Workspace of attn_bwd_varlen: H * total_q floats for D, rounded up to 256
+ * bytes (0 if p is invalid).  With ATTN_BWD_D_PRECOMPUTED it must hold D =
+ * rowsum(dO * O) in [H, total_q] order: attn_bwd_preprocess with the problem
+ * {B = 1, H, Nq = total_q, Nkv = 1, d} on the packed o and dout writes it. */
+size_t attn_bwd_varlen_workspace_bytes(const attn_varlen* p);
+
+/* Backward of attn_fwd_varlen; arguments and flags as attn_bwd (dq F32 and
+ * added to under ATTN_BWD_DQ_ACCUMULATE). */
+attn_status attn_bwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                            attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
+                            attn_tensor dk, attn_tensor dv, void* workspace,
+                            size_t workspace_bytes, uint32_t flags, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(attn_status st);
 

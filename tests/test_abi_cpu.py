@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_abi_version", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes",
-        "attn_fwd", "attn_fwd_chunked", "attn_lse_merge", "attn_status_string"])
+        "attn_fwd", "attn_fwd_chunked", "attn_lse_merge", "attn_status_string",
+        "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -163,3 +164,45 @@ def test_preprocess_validation(lib):
     assert call(o=T(ptr=0)) == INVALID
     assert call(o=T(dtype=1), dout=T(dtype=0)) == INVALID   # f32 dO needs an f32 O
     assert call(p=P(d=40)) == UNSUPPORTED
+
+
+def VL(n_seq=3, H=4, d=64, max_q=200, max_kv=200, total_q=500, total_kv=500, scale=0.125,
+       cu_q=FAKE, cu_kv=FAKE):
+    return ebw._Varlen(n_seq, H, d, max_q, max_kv, total_q, total_kv, scale, cu_q, cu_kv)
+
+
+def PT(ptr=FAKE, dtype=1, sh=64, sn=4 * 64):
+    return ebw._Tensor(ptr, dtype, 0, sh, sn)
+
+
+def test_varlen_validation(lib):
+    def fwd_v(p=None, q=None, lse=FAKE):
+        return lib.attn_fwd_varlen(None if p is False else ctypes.byref(p or VL()), q or PT(),
+                                   PT(), PT(), PT(), lse, None)
+    assert fwd_v(p=False) == INVALID
+    assert fwd_v(p=VL(n_seq=0)) == INVALID
+    assert fwd_v(p=VL(max_q=0)) == INVALID
+    assert fwd_v(p=VL(total_q=-1)) == INVALID
+    assert fwd_v(p=VL(cu_q=0)) == INVALID
+    assert fwd_v(p=VL(cu_kv=0)) == INVALID
+    assert fwd_v(p=VL(cu_q=FAKE + 2)) == UNSUPPORTED
+    assert fwd_v(p=VL(d=96)) == UNSUPPORTED
+    assert fwd_v(p=VL(scale=float("inf"))) == INVALID
+    assert fwd_v(lse=0) == INVALID
+    assert fwd_v(q=PT(dtype=0)) == INVALID                       # mixed dtypes
+    assert lib.attn_fwd_varlen(ctypes.byref(VL()), PT(dtype=0), PT(dtype=0), PT(dtype=0),
+                               PT(dtype=0), FAKE, None) == UNSUPPORTED   # fp32: bf16 only
+    # workspace: H * total_q floats for D, rounded up to 256 bytes
+    assert lib.attn_bwd_varlen_workspace_bytes(ctypes.byref(VL(H=4, total_q=500))) == 8192
+    assert lib.attn_bwd_varlen_workspace_bytes(ctypes.byref(VL(n_seq=0))) == 0
+
+    def bwd_v(flags=0, ws=FAKE, ws_bytes=8192, p=None):
+        return lib.attn_bwd_varlen(ctypes.byref(p or VL()), PT(), PT(), PT(), PT(), PT(), FAKE,
+                                   PT(), PT(), PT(), ws, ws_bytes, flags, None)
+    assert bwd_v(ws_bytes=8191) == WORKSPACE
+    assert bwd_v(ws=0) == WORKSPACE
+    assert bwd_v(ws=FAKE + 16) == WORKSPACE                      # not 256-byte aligned
+    assert bwd_v(flags=4 | 8) == INVALID                         # NO_DQ and NO_DKDV
+    assert bwd_v(flags=16) == INVALID
+    assert bwd_v(flags=1) == INVALID                             # accumulate needs fp32 dq
+    assert bwd_v(p=VL(max_kv=-3)) == INVALID
