@@ -66,7 +66,9 @@ def build(verbose: bool = False, out_dir: str | None = None,
                 print(out)
     lib = os.path.join(out_dir, "libexattn.so") if out_dir else LIB
     tmp = lib + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp])
+    # every symbol resolved at link time: a missing definition fails the build
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined",
+          *[o for o, _ in jobs], "-o", tmp])
     os.replace(tmp, lib)
     if verbose:
         print(f"built {lib}")

@@ -862,24 +862,53 @@ void dq_bf16_kernel(BwdArgs a, int accumulate) {
 }
 
 // --------------------------------------------------------------------------
-// fp32 inputs: genuine fp32 arithmetic, exact library exp.  Not tuned.
-//  - dK, dV: one lane per key row (its K, V rows in padded LDS, its dK, dV
-//    accumulators in registers), query tiles of 16 rows read by broadcast.
-//  - dQ: one lane per query row (its Q, dO rows in padded LDS, dQ in
-//    registers), key tiles of 16 rows read by broadcast.
+// fp32 inputs: genuine fp32 arithmetic, exact library exp.  As in the fp32
+// forward, a workgroup owns 64 rows (one per lane, the same rows in each of
+// its W waves) and splits the streamed rows over the waves; the waves'
+// partial gradients are summed through LDS at the end.
+//  - dK, dV: owned key rows (K, V in padded LDS, dK, dV in registers),
+//    streamed query tiles read by broadcast.
+//  - dQ: owned query rows (Q, dO in padded LDS, dQ in registers), streamed
+//    key tiles read by broadcast.
 // --------------------------------------------------------------------------
 namespace bwdf {
-constexpr int RB = 32;  // rows owned per workgroup (one per lane)
-constexpr int TB = 16;  // streamed tile rows
+constexpr int RB = 64;      // owned rows per workgroup, one per lane
+constexpr int TB = 2;       // streamed rows per wave per staged tile
+// waves splitting the streamed rows: eight where two waves per SIMD keep
+// their accumulators in registers, else four (one per SIMD: the dK + dV
+// accumulators, 2d registers, need the larger register file)
+template <int D, bool DKDV = false>
+constexpr int waves() { return D <= 80 && !DKDV ? 8 : 4; }
 }  // namespace bwdf
 
+// x[lane] of every wave summed into wave 0's x (buf: [RB][D + 1] floats)
+template <int W, int D>
+__device__ __forceinline__ void sum_over_waves(float (&x)[D], float (*buf)[D + 1], int w,
+                                               int lane) {
+  for (int r = 1; r < W; ++r) {
+    __syncthreads();
+    if (w == r) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) buf[lane][i] = x[i];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) x[i] += buf[lane][i];
+    }
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(bwdf::RB) void bwd_f32_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__((64 * bwdf::waves<D, true>())) void bwd_f32_dkdv_kernel(BwdArgs a) {
   using namespace bwdf;
+  constexpr int W = waves<D, true>(), BS = W * TB;  // BS: streamed rows per staged tile
   __shared__ float Kown[RB][D + 1], Vown[RB][D + 1];
-  __shared__ float Qt[TB][D], dOt[TB][D];
-  __shared__ float lse_t[TB], D_t[TB];
-  const int tid = threadIdx.x;
+  __shared__ float Qt[BS][D], dOt[BS][D];
+  __shared__ float lse_t[BS], D_t[BS];
+  __shared__ float Ab[RB][D + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nkb = (a.Nkv + RB - 1) / RB;
   const int kb = blockIdx.x % nkb;
   const int bh = blockIdx.x / nkb;
@@ -891,7 +920,7 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dkdv_kernel(BwdArgs a) {
   const float* lsep = a.lse + ((int64_t)b * a.H + h) * a.Nq;
   const float* dsp = a.dsum + ((int64_t)b * a.H + h) * a.Nq;
   const int k0 = kb * RB;
-  for (int e = tid; e < RB * D; e += RB) {
+  for (int e = tid; e < RB * D; e += 64 * W) {
     const int r = e / D, cc = e % D;
     const bool ok = k0 + r < a.Nkv;
     Kown[r][cc] = ok ? kp[(int64_t)(k0 + r) * a.ks.sn + cc] : 0.f;
@@ -900,28 +929,32 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dkdv_kernel(BwdArgs a) {
   float dk[D], dv[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) dk[i] = dv[i] = 0.f;
-  for (int q0 = 0; q0 < a.Nq; q0 += TB) {
+  for (int q0 = 0; q0 < a.Nq; q0 += BS) {
     __syncthreads();
-    for (int e = tid; e < TB * D; e += RB) {
+    for (int e = tid; e < BS * D; e += 64 * W) {
       const int r = e / D, cc = e % D;
       const bool ok = q0 + r < a.Nq;
       Qt[r][cc] = ok ? qp[(int64_t)(q0 + r) * a.qs.sn + cc] : 0.f;
       dOt[r][cc] = ok ? dop[(int64_t)(q0 + r) * a.dos.sn + cc] : 0.f;
     }
-    if (tid < TB) {
+    if (tid < BS) {
       const bool ok = q0 + tid < a.Nq;
       lse_t[tid] = ok ? lsep[q0 + tid] : INFINITY;
       D_t[tid] = ok ? dsp[q0 + tid] : 0.f;
     }
     __syncthreads();
-    for (int j = 0; j < TB; ++j) {
-      float s = 0.f, dpv = 0.f;
+#pragma unroll 1
+    for (int t = 0; t < TB; ++t) {
+      const int j = w * TB + t;  // rows past Nq: Q = dO = 0, LSE = +inf, so P = 0
+      float s4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < D; ++i) {
-        s = fmaf(Qt[j][i], Kown[tid][i], s);
-        dpv = fmaf(dOt[j][i], Vown[tid][i], dpv);
+        s4[i & 3] = fmaf(Qt[j][i], Kown[lane][i], s4[i & 3]);
+        p4[i & 3] = fmaf(dOt[j][i], Vown[lane][i], p4[i & 3]);
       }
-      const float p = expf(s * a.scale - lse_t[j]);
+      const float sv = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      const float dpv = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      const float p = expf(sv * a.scale - lse_t[j]);
       const float ds = p * (dpv - D_t[j]);
 #pragma unroll
       for (int i = 0; i < D; ++i) {
@@ -930,8 +963,10 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dkdv_kernel(BwdArgs a) {
       }
     }
   }
-  const int kr = k0 + tid;
-  if (kr >= a.Nkv) return;
+  sum_over_waves<W, D>(dk, Ab, w, lane);
+  sum_over_waves<W, D>(dv, Ab, w, lane);
+  const int kr = k0 + lane;
+  if (w != 0 || kr >= a.Nkv) return;
   float* dkp = (float*)a.dk + b * a.dks.sb + h * a.dks.sh + (int64_t)kr * a.dks.sn;
   float* dvp = (float*)a.dv + b * a.dvs.sb + h * a.dvs.sh + (int64_t)kr * a.dvs.sn;
   for (int i = 0; i < D; ++i) {
@@ -941,11 +976,15 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dkdv_kernel(BwdArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(bwdf::RB) void bwd_f32_dq_kernel(BwdArgs a, int accumulate) {
+__global__ __launch_bounds__(64 * bwdf::waves<D>()) void bwd_f32_dq_kernel(BwdArgs a,
+                                                                       int accumulate) {
   using namespace bwdf;
+  constexpr int W = waves<D>(), BS = W * TB;
   __shared__ float Qown[RB][D + 1], dOown[RB][D + 1];
-  __shared__ float Kt[TB][D], Vt[TB][D];
-  const int tid = threadIdx.x;
+  __shared__ float Kt[BS][D], Vt[BS][D];
+  __shared__ float Ab[RB][D + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqb = (a.Nq + RB - 1) / RB;
   const int qb = blockIdx.x % nqb;
   const int bh = blockIdx.x / nqb;
@@ -955,43 +994,48 @@ __global__ __launch_bounds__(bwdf::RB) void bwd_f32_dq_kernel(BwdArgs a, int acc
   const float* kp = (const float*)a.k + b * a.ks.sb + h * a.ks.sh;
   const float* vp = (const float*)a.v + b * a.vs.sb + h * a.vs.sh;
   const int q0 = qb * RB;
-  for (int e = tid; e < RB * D; e += RB) {
+  for (int e = tid; e < RB * D; e += 64 * W) {
     const int r = e / D, cc = e % D;
     const bool ok = q0 + r < a.Nq;
     Qown[r][cc] = ok ? qp[(int64_t)(q0 + r) * a.qs.sn + cc] : 0.f;
     dOown[r][cc] = ok ? dop[(int64_t)(q0 + r) * a.dos.sn + cc] : 0.f;
   }
-  const int qi = q0 + tid;
+  const int qi = q0 + lane;
   const bool qvalid = qi < a.Nq;
   const float lse_i = qvalid ? a.lse[((int64_t)b * a.H + h) * a.Nq + qi] : INFINITY;
   const float D_i = qvalid ? a.dsum[((int64_t)b * a.H + h) * a.Nq + qi] : 0.f;
   float dq[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) dq[i] = 0.f;
-  for (int j0 = 0; j0 < a.Nkv; j0 += TB) {
+  for (int j0 = 0; j0 < a.Nkv; j0 += BS) {
     __syncthreads();
-    for (int e = tid; e < TB * D; e += RB) {
+    for (int e = tid; e < BS * D; e += 64 * W) {
       const int r = e / D, cc = e % D;
       const bool ok = j0 + r < a.Nkv;
       Kt[r][cc] = ok ? kp[(int64_t)(j0 + r) * a.ks.sn + cc] : 0.f;
       Vt[r][cc] = ok ? vp[(int64_t)(j0 + r) * a.vs.sn + cc] : 0.f;
     }
     __syncthreads();
-    const int nj = min(TB, a.Nkv - j0);
-    for (int j = 0; j < nj; ++j) {
-      float s = 0.f, dpv = 0.f;
+#pragma unroll 1
+    for (int t = 0; t < TB; ++t) {
+      const int j = w * TB + t;
+      if (j0 + j >= a.Nkv) continue;  // (uniform) keys past the end
+      float s4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < D; ++i) {
-        s = fmaf(Qown[tid][i], Kt[j][i], s);
-        dpv = fmaf(dOown[tid][i], Vt[j][i], dpv);
+        s4[i & 3] = fmaf(Qown[lane][i], Kt[j][i], s4[i & 3]);
+        p4[i & 3] = fmaf(dOown[lane][i], Vt[j][i], p4[i & 3]);
       }
-      const float p = expf(s * a.scale - lse_i);
+      const float sv = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      const float dpv = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      const float p = expf(sv * a.scale - lse_i);
       const float ds = p * (dpv - D_i);
 #pragma unroll
       for (int i = 0; i < D; ++i) dq[i] = fmaf(ds, Kt[j][i], dq[i]);
     }
   }
-  if (!qvalid) return;
+  sum_over_waves<W, D>(dq, Ab, w, lane);
+  if (w != 0 || !qvalid) return;
   float* dqp = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)qi * a.dqs.sn;
   for (int i = 0; i < D; ++i) {
     const float v = dq[i] * a.scale;
@@ -1128,13 +1172,14 @@ static hipError_t bwd_f32_d(const BwdArgs& a, int do_dkdv, int do_dq, int accumu
   const long long gq = (long long)((a.Nq + bwdf::RB - 1) / bwdf::RB) * a.H * a.B;
   if (gk > 0x7fffffffLL || gq > 0x7fffffffLL) return hipErrorInvalidValue;
   if (do_dkdv) {
-    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D>), dim3((unsigned)gk), dim3(bwdf::RB), 0, s, a);
+    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D>), dim3((unsigned)gk),
+                       dim3(64 * bwdf::waves<D, true>()), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (do_dq) {
-    hipLaunchKernelGGL((bwd_f32_dq_kernel<D>), dim3((unsigned)gq), dim3(bwdf::RB), 0, s, a,
-                       accumulate);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D>), dim3((unsigned)gq), dim3(64 * bwdf::waves<D>()),
+                       0, s, a, accumulate);
     return hipGetLastError();
   }
   return hipSuccess;

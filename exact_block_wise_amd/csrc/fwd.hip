@@ -286,21 +286,35 @@ void fwd_bf16_kernel(FwdArgs a) {
 
 // --------------------------------------------------------------------------
 // fp32 inputs: genuine fp32 products and sums on the vector ALUs, exact
-// library exp/log.  One lane per query row; key/value tiles of 32 rows in
-// LDS are read by broadcast.  Meant for small problems that need fp32
-// accuracy; it is not tuned.
+// library exp/log.  Meant for small problems that need fp32 accuracy, where
+// a workgroup per 64 query rows alone would leave the chip almost empty, so
+// each workgroup splits its key range over W waves: every lane owns one
+// query row in every wave, the waves take disjoint keys of each staged tile
+// and run their own online softmax, and the W partial (m, l, O) are merged
+// exactly at the end (the LSE merge of the LV-XAttn abstract, over waves).
 // --------------------------------------------------------------------------
 namespace fwdf {
-constexpr int BM = 64;
-constexpr int BN = 32;
+constexpr int BM = 64;      // query rows per workgroup, one per lane
+constexpr int TB = 4;       // keys per wave per staged tile
+// waves splitting the keys: eight (two per SIMD) up to d = 80, four at 128
+template <int D>
+constexpr int waves() { return D <= 80 ? 8 : 4; }
 }  // namespace fwdf
 
 template <int D>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * fwdf::waves<D>()) void fwd_f32_kernel(FwdArgs a) {
   using namespace fwdf;
+  constexpr int W = waves<D>(), BN = W * TB;  // BN: keys per staged tile
   __shared__ float Ks[BN][D];
   __shared__ float Vs[BN][D];
-  const int tid = threadIdx.x;
+  __shared__ float Ms[BM], Ls[BM];
+  __shared__ float Ab[BM][D + 1];  // a partial O being merged (padded rows)
+  // the query rows stay in registers up to d = 80; at d = 128 they and the
+  // accumulator would not both fit, so the rows are read from LDS
+  constexpr bool QREG = D <= 80;
+  __shared__ float Qs[QREG ? 1 : BM][D + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqb = (a.Nq + BM - 1) / BM;
   int idx = blockIdx.x;
   const int qb = idx % nqb;
@@ -315,49 +329,84 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   const float* qp = (const float*)a.q + b * a.qs.sb + h * a.qs.sh;
   const float* kp = (const float*)a.k + b * a.ks.sb + h * a.ks.sh + (int64_t)kv_lo * a.ks.sn;
   const float* vp = (const float*)a.v + b * a.vs.sb + h * a.vs.sh + (int64_t)kv_lo * a.vs.sn;
-  const int qrow = qb * BM + tid;
+  const int qrow = qb * BM + lane;
   const bool qvalid = qrow < a.Nq;
 
-  float qv[D], acc[D];
+  float qv[QREG ? D : 1], acc[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    qv[i] = qvalid ? qp[(int64_t)qrow * a.qs.sn + i] : 0.f;
+    if constexpr (QREG) qv[i] = qvalid ? qp[(int64_t)qrow * a.qs.sn + i] : 0.f;
     acc[i] = 0.f;
   }
+  if constexpr (!QREG) {
+    for (int e = tid; e < BM * D; e += 64 * W) {
+      const int r = e / D, cc = e % D;
+      Qs[r][cc] = qb * BM + r < a.Nq ? qp[(int64_t)(qb * BM + r) * a.qs.sn + cc] : 0.f;
+    }
+  }
+  auto qval = [&](int i) -> float {
+    if constexpr (QREG) return qv[i];
+    else return Qs[lane][i];
+  };
   float m = -INFINITY, l = 0.f;
   for (int j0 = 0; j0 < n_kv; j0 += BN) {
     __syncthreads();
-    for (int e = tid; e < BN * D; e += 64) {
+    for (int e = tid; e < BN * D; e += 64 * W) {
       const int r = e / D, cc = e % D;
       const bool ok = j0 + r < n_kv;
       Ks[r][cc] = ok ? kp[(int64_t)(j0 + r) * a.ks.sn + cc] : 0.f;
       Vs[r][cc] = ok ? vp[(int64_t)(j0 + r) * a.vs.sn + cc] : 0.f;
     }
     __syncthreads();
-    const int nj = min(BN, n_kv - j0);
-    float sc[BN];
+    if (j0 + w * TB >= n_kv) continue;  // this wave's keys of the tile are all past the end
+    float sc[TB];
     float mx = -INFINITY;
-    for (int j = 0; j < BN; ++j) {
-      float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < D; ++i) dot = fmaf(qv[i], Ks[j][i], dot);
-      sc[j] = j < nj ? dot * a.scale : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
+    for (int t = 0; t < TB; ++t) {
+      const int j = w * TB + t;
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < D; ++i) d4[i & 3] = fmaf(qval(i), Ks[j][i], d4[i & 3]);
+      sc[t] = j0 + j < n_kv ? ((d4[0] + d4[1]) + (d4[2] + d4[3])) * a.scale : -INFINITY;
+      mx = fmaxf(mx, sc[t]);
     }
-    const float m_new = fmaxf(m, mx);
+    const float m_new = fmaxf(m, mx);  // finite: key w * TB of the tile exists
     const float alpha = expf(m - m_new);
     l *= alpha;
 #pragma unroll
     for (int i = 0; i < D; ++i) acc[i] *= alpha;
-    for (int j = 0; j < BN; ++j) {
-      const float p = expf(sc[j] - m_new);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const float p = expf(sc[t] - m_new);
       l += p;
 #pragma unroll
-      for (int i = 0; i < D; ++i) acc[i] = fmaf(p, Vs[j][i], acc[i]);
+      for (int i = 0; i < D; ++i) acc[i] = fmaf(p, Vs[w * TB + t][i], acc[i]);
     }
     m = m_new;
   }
-  if (!qvalid) return;
+  // merge the waves' partials into wave 0, one wave at a time
+  for (int r = 1; r < W; ++r) {
+    __syncthreads();
+    if (w == r) {
+      Ms[lane] = m;
+      Ls[lane] = l;
+#pragma unroll
+      for (int i = 0; i < D; ++i) Ab[lane][i] = acc[i];
+    }
+    __syncthreads();
+    if (w == 0) {
+      const float mo = Ms[lane];
+      const float mn = fmaxf(m, mo);
+      if (mn != -INFINITY) {  // both empty: nothing to merge
+        const float a0 = expf(m - mn), a1 = expf(mo - mn);
+        l = l * a0 + Ls[lane] * a1;
+#pragma unroll
+        for (int i = 0; i < D; ++i) acc[i] = acc[i] * a0 + Ab[lane][i] * a1;
+        m = mn;
+      }
+    }
+  }
+  if (w != 0 || !qvalid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int64_t orow = (int64_t)c * a.o_chunk_stride + b * a.os.sb + h * a.os.sh +
                        (int64_t)qrow * a.os.sn;
@@ -395,7 +444,8 @@ static hipError_t fwd_f32_d(const FwdArgs& a, hipStream_t s) {
   const int nqb = (a.Nq + fwdf::BM - 1) / fwdf::BM;
   const long long grid = (long long)nqb * a.H * a.B * a.n_chunks;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)grid), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)grid), dim3(64 * fwdf::waves<D>()), 0, s,
+                     a);
   return hipGetLastError();
 }
 
