@@ -226,8 +226,9 @@ def cpu_baseline(w, budget_s):
         heads += 1
     return {"value": round(flops / t_work / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {len(order)} heads (sequence, head) of {w.name}, fwd+bwd in "
-                      f"fp64 NumPy, {t_work:.1f} s"}
+            "sample": f"{heads} of {len(order)} heads " +
+                      ("(sequence, head)" if is_packed(w) else "(b, h)") +
+                      f" of {w.name}, fwd+bwd in fp64 NumPy, {t_work:.1f} s"}
 
 
 def main():
