@@ -27,6 +27,8 @@ attn_status check_problem(const attn_problem* p) {
   if (p->B < 1 || p->H < 1 || p->Nq < 1 || p->Nkv < 1 || p->d < 1) return ATTN_E_INVALID;
   if (!isfinite(p->scale)) return ATTN_E_INVALID;
   if (!supported_d(p->d)) return ATTN_E_UNSUPPORTED;
+  // kernels index (batch, head) pairs with 32-bit integers
+  if ((int64_t)p->B * p->H > INT32_MAX) return ATTN_E_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -77,6 +79,7 @@ attn_status check_varlen(const attn_varlen* p) {
   if (p->total_q < 0 || p->total_kv < 0 || !p->cu_q || !p->cu_kv) return ATTN_E_INVALID;
   if (!isfinite(p->scale)) return ATTN_E_INVALID;
   if (!supported_d(p->d)) return ATTN_E_UNSUPPORTED;
+  if ((int64_t)p->n_seq * p->H > INT32_MAX) return ATTN_E_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(p->cu_q) % 4 || reinterpret_cast<uintptr_t>(p->cu_kv) % 4)
     return ATTN_E_UNSUPPORTED;
   // the statistics index h * total_q + t and the grid must fit their types

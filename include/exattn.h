@@ -34,7 +34,8 @@
  *    distinct streams may run concurrently from different host threads.
  *  - Supported: d in {64, 80, 128}; inputs all F32 or all BF16.  bf16 inputs
  *    use bf16 matrix-core products with fp32 accumulation; f32 inputs use
- *    genuine fp32 products and accumulation.
+ *    genuine fp32 products and accumulation.  B*H (or sequences * H for
+ *    packed sequences) at most 2^31 - 1, else ATTN_E_UNSUPPORTED.
  */
 #ifndef EXATTN_H
 #define EXATTN_H

@@ -88,6 +88,7 @@ def test_fwd_validation(lib):
     assert fwd(lib, o=T(sh=-64)) == INVALID
     assert fwd(lib, lse=FAKE + 2) == UNSUPPORTED
     assert fwd(lib, k=T(sn=(1 << 23) + 8)) == UNSUPPORTED  # row stride above 16 MiB
+    assert fwd(lib, p=P(B=1 << 16, H=1 << 15)) == UNSUPPORTED  # B*H past 32-bit indexing
 
 
 def test_fwd_chunked_validation(lib):
@@ -206,3 +207,4 @@ def test_varlen_validation(lib):
     assert bwd_v(flags=16) == INVALID
     assert bwd_v(flags=1) == INVALID                             # accumulate needs fp32 dq
     assert bwd_v(p=VL(max_kv=-3)) == INVALID
+    assert fwd_v(p=VL(n_seq=1 << 20, H=1 << 12)) == UNSUPPORTED  # sequences * heads too many
