@@ -298,3 +298,49 @@ def test_full_size_workload(name):
                            f"{name}[{b},{h}]")
         _say(f"  head ({b},{h}) grad errors {['%.2e' % e for e in errs]}")
     assert max(errs) < TOL_GRAD_FRO
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_chunked_forward_merge_backward(d):
+    """fp32 inputs through the chunked forward (the wave-split fp32 kernel
+    with a chunk grid dimension), the merge and a chunk-by-chunk backward
+    with fp32 dQ accumulation, against the unsplit oracle at the fp32
+    tolerance."""
+    B, H, Nq, Nkv, n_chunks = 1, 2, 70, 250, 3
+    x = synth.random_case(2000 + d, B, H, Nq, Nkv, d, "f32")
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q, k, v, do = (to_dev(x[n], "f32") for n in ("q", "k", "v", "do"))
+    o_parts, lse_parts = ebw.fwd_chunked(q, k, v, n_chunks, scale=scale)
+    o, lse = ebw.lse_merge(o_parts, lse_parts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], scale)
+    check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "f32", "fp32 merged")
+    L = -(-Nkv // n_chunks)
+    dq = torch.zeros((B, H, Nq, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ebw.bwd_workspace_bytes(q, k) // 4, dtype=torch.float32, device="cuda")
+    ebw.bwd_preprocess(o, do, ws)
+    for c in range(n_chunks):
+        lo, hi = c * L, min((c + 1) * L, Nkv)
+        ebw.bwd(q, k[:, :, lo:hi], v[:, :, lo:hi], None, do, lse, scale=scale, dq=dq,
+                dk=dk[:, :, lo:hi], dv=dv[:, :, lo:hi], accumulate_dq=True, workspace=ws,
+                d_precomputed=True)
+    torch.cuda.synchronize()
+    ref = oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale)
+    check_grads([to_host(t) for t in (dq, dk, dv)], ref, "f32", "fp32 chunked")
+
+
+def test_fp32_bwd_flags():
+    """fp32: the NO_DQ / NO_DKDV halves with a precomputed D give the bits of
+    the full call."""
+    x = synth.random_case(2100, 2, 2, 150, 90, 80, "f32")
+    q, k, v, do = (to_dev(x[n], "f32") for n in ("q", "k", "v", "do"))
+    o, lse = ebw.fwd(q, k, v)
+    full = ebw.bwd(q, k, v, o, do, lse)
+    ws = torch.empty(ebw.bwd_workspace_bytes(q, k) // 4, dtype=torch.float32, device="cuda")
+    ebw.bwd_preprocess(o, do, ws)
+    dq, _, _ = ebw.bwd(q, k, v, None, do, lse, workspace=ws, d_precomputed=True, need_dkdv=False)
+    _, dk, dv = ebw.bwd(q, k, v, None, do, lse, workspace=ws, d_precomputed=True, need_dq=False)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(full, (dq, dk, dv)):
+        assert torch.equal(a_, b_)
