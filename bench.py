@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for the HBM "
                          "counter scale factors)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time only plain bf16 GEMMs through the vendor library (torch.matmul / "
+                         "hipBLASLt): the matrix-core rate this GPU sustains outside attention")
     ap.add_argument("--make-traffic-profile", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
                     "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results of a bench run "
@@ -97,6 +100,33 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES}))
+
+
+def gemm_ceiling():
+    """Sustained bf16 rate of plain square GEMMs through the vendor library
+    (torch.matmul, hipBLASLt on ROCm), timed with HIP events: the practical
+    matrix-core ceiling of this GPU next to the published dense peak."""
+    import torch
+    torch.manual_seed(0)
+    out = {}
+    for n in (4096, 8192, 16384):
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        it = 20 if n == 16384 else 50
+        for _ in range(5):
+            a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(it):
+            a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / it
+        out[f"gemm_{n}"] = {"ms": round(ms, 4), "tflops": round(2 * n ** 3 / ms / 1e9, 1),
+                            "frac_of_peak": round(2 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 3)}
+        del a, b
+    print(json.dumps({"gemm_ceiling_bf16": out, "peak_tflops": PEAK_BF16_TFLOPS}))
 
 
 def _pmc_per_dispatch(d, counter, name_part):
@@ -238,6 +268,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

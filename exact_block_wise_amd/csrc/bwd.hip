@@ -693,18 +693,21 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
 
   // One key/value tile; NEXT: tile it + 1 exists and is staged into the
   // other buffer while this one is computed (waited for before the barrier).
-  auto tile = [&](auto next_tag, int it) {
+  // NCB = 1: a last tile of at most 32 keys, whose second 32-key block would
+  // add nothing (its K rows are zero), is left out.
+  auto tile = [&](auto next_tag, auto ncb_tag, int it) {
     constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr int NCB = decltype(ncb_tag)::value;
     const int buf = it & 1;
     if (NEXT) load_tile((it + 1) * BN, buf ^ 1);
     if (wave_active) {
       const bf16* Kt = lds + buf * 2 * L::tile;
       const bf16* Vt = Kt + L::tile;
-      f32x16 st[2][NQB], dpt[2][NQB];
+      f32x16 st[NCB][NQB], dpt[NCB][NQB];
       // the tile's K and V operands (A operands of S^T and dP^T)
-      bf16x8 ka[2][KC], va[2][KC];
+      bf16x8 ka[NCB][KC], va[NCB][KC];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           ka[cb][kc] = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
@@ -712,7 +715,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
         }
       prio_mfma();
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           st[cb][qb] = f32x16{};
@@ -729,7 +732,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       }
       prio_valu();
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -741,7 +744,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       // (0..3) and 16t + 8 + 4g + (0..3) = accumulator entries 8hh..8hh+7)
       prio_mfma();
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2 * NCB; ++t) {
         bf16x8 sa[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) sa[qb] = acc_half_to_bf16(st[t >> 1][qb], t & 1);
@@ -762,9 +765,14 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     load_tile(0, 0);
     wait_vmem();
     __syncthreads();
+    using Full = std::integral_constant<int, 2>;
+    using Half = std::integral_constant<int, 1>;
     int it = 0;
-    for (; it + 1 < ntiles; ++it) tile(std::true_type{}, it);
-    tile(std::false_type{}, it);
+    for (; it + 1 < ntiles; ++it) tile(std::true_type{}, Full{}, it);
+    if (n_kv - it * BN > 32)
+      tile(std::false_type{}, Full{}, it);
+    else
+      tile(std::false_type{}, Half{}, it);
   }
 
   if (!wave_active) return;

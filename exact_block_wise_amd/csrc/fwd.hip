@@ -148,12 +148,19 @@ void fwd_bf16_kernel(FwdArgs a) {
       const bf16* Vt = Kt + L::tile;
       // S^T = K Q^T for two 32-key blocks x NQB query blocks; keys past the
       // end weigh nothing
+      // (a last tile of at most 32 keys skips the second key block's
+      // products; its scores stay zero and are masked below, and the value
+      // products of 16-key chunks past the end are skipped too)
+      const int rem = n_kv - j0;
+      const bool second = !TAIL || rem > 32;
+      const int nchunks = TAIL ? (rem + 15) / 16 : 4;
       f32x16 s[2][NQB];
       prio_mfma();
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+        if (cb == 1 && !second) break;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
@@ -227,6 +234,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       prio_mfma();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
+        if (t >= nchunks) break;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const bf16x8 va = tr_operand(Vt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
