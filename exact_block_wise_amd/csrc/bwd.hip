@@ -225,37 +225,52 @@ __device__ __forceinline__ void negate_rows(bf16x8 (&v)[NCB][KC]) {
 }
 
 // dK and dV of a wave's keys kw .. kw + 32 NCB - 1 from the transposed
-// accumulators (dk holds -dK / scale, see dkdv_qblock): lane owns key
+// accumulators (dk holds -dK / scale, see dkdv_qblock).  A lane owns key
 // kw + 32cb + ln and, per 32-column block db, the runs d = 32db + 8i + 4g +
-// (0..3) (accumulator entries 4i .. 4i+3), each written as one 8-byte store.
+// (0..3) (accumulator entries 4i .. 4i+3).  Stored from there, every wave
+// store instruction would touch 32 rows with 16 bytes each, one L2 request
+// per 16 bytes; instead the runs go to this wave's LDS staging rows
+// (`stage`, 32 NCB rows of stride DP + 8) and whole rows are read back and
+// leave in 16-byte stores, so each instruction writes contiguous row memory.
+// The staging rows are this wave's alone and LDS operations of one wave
+// complete in order, so no barrier is needed.
 template <int D, int NCB>
 __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, const SeqSpan& sp,
                                            int kw, const f32x16 (&dk)[NCB][(D + 31) / 32],
-                                           const f32x16 (&dv)[NCB][(D + 31) / 32], int lane) {
-  constexpr int NDB = (D + 31) / 32;
+                                           const f32x16 (&dv)[NCB][(D + 31) / 32], bf16* stage,
+                                           int lane) {
+  constexpr int NDB = (D + 31) / 32, SRS = NDB * 32 + 8, PPR = D / 8;
+  constexpr int NP = 32 * NCB * PPR / 64;  // 16-byte pieces per lane and tensor
+  static_assert(32 * NCB * PPR % 64 == 0, "whole wave instructions");
   const int ln = lane & 31, g = lane >> 5;
-  const float ks = -a.scale;
-  bf16* dkp = (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh + (int64_t)sp.kv_row0 * a.dks.sn;
-  bf16* dvp = (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh + (int64_t)sp.kv_row0 * a.dvs.sn;
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int kr = kw + 32 * cb + ln;
-    if (kr >= sp.nkv) continue;
+  for (int t = 0; t < 2; ++t) {  // dK, then dV
+    const f32x16 (&acc)[NCB][NDB] = t == 0 ? dk : dv;
+    const float sc = t == 0 ? -a.scale : 1.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = 32 * db + 8 * i + 4 * g;
-        if (d0 >= D) continue;
-        const f32x16& k16 = dk[cb][db];
-        const f32x16& v16 = dv[cb][db];
-        const bf16x4 k4 = {(bf16)(k16[4 * i] * ks), (bf16)(k16[4 * i + 1] * ks),
-                           (bf16)(k16[4 * i + 2] * ks), (bf16)(k16[4 * i + 3] * ks)};
-        const bf16x4 v4 = {(bf16)v16[4 * i], (bf16)v16[4 * i + 1], (bf16)v16[4 * i + 2],
-                           (bf16)v16[4 * i + 3]};
-        *reinterpret_cast<bf16x4*>(dkp + (int64_t)kr * a.dks.sn + d0) = k4;
-        *reinterpret_cast<bf16x4*>(dvp + (int64_t)kr * a.dvs.sn + d0) = v4;
-      }
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = 32 * db + 8 * i + 4 * g;
+          if (d0 >= D) continue;
+          const f32x16& x = acc[cb][db];
+          const bf16x4 r4 = {(bf16)(x[4 * i] * sc), (bf16)(x[4 * i + 1] * sc),
+                             (bf16)(x[4 * i + 2] * sc), (bf16)(x[4 * i + 3] * sc)};
+          *reinterpret_cast<bf16x4*>(&stage[(32 * cb + ln) * SRS + d0]) = r4;
+        }
+    bf16* out = t == 0 ? (bf16*)a.dk + b * a.dks.sb + h * a.dks.sh +
+                             (int64_t)(sp.kv_row0 + kw) * a.dks.sn
+                       : (bf16*)a.dv + b * a.dvs.sb + h * a.dvs.sh +
+                             (int64_t)(sp.kv_row0 + kw) * a.dvs.sn;
+    const int64_t sn = t == 0 ? a.dks.sn : a.dvs.sn;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int e = 64 * j + lane, r = e / PPR, pc = e % PPR;
+      const bf16x8 v = load_bf16x8(&stage[r * SRS + 8 * pc]);
+      if (kw + r < sp.nkv) *reinterpret_cast<bf16x8*>(out + (int64_t)r * sn + 8 * pc) = v;
+    }
   }
 }
 
@@ -391,7 +406,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 
   if (!wave_active) return;
   if constexpr (kPinAcc) agpr_results_ready();
-  dkdv_store<D, NCB>(a, b, h, sp, kw, dk, dv, lane);
+  // the query tiles are free after the last tile's barrier: they stage the
+  // output rows (32 NCB rows of stride RS per wave)
+  static_assert(4 * 32 * NCB <= 4 * BM, "staging fits the query tiles");
+  dkdv_store<D, NCB>(a, b, h, sp, kw, dk, dv, lds + w * 32 * NCB * RS, lane);
 }
 
 // --------------------------------------------------------------------------
@@ -417,7 +435,8 @@ template <int D>
 struct ResLds {
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int RS = DP + 8;                           // row stride of Q, dO
-  static constexpr int bytes = 2 * resk::QR * RS * 2 + 2 * resk::QR * 4;
+  static constexpr int stage = 32 * RS;                       // output rows per wave
+  static constexpr int bytes = 2 * resk::QR * RS * 2 + 2 * resk::QR * 4 + 4 * stage * 2;
 };
 
 #ifndef EXATTN_DKDV_RESIDENT
@@ -439,6 +458,7 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, g = lane >> 5;
+  bf16* const stage = reinterpret_cast<bf16*>(Ds + QR) + w * L::stage;  // this wave's output rows
 
   int idx = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = idx % groups;
@@ -508,7 +528,7 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
     for (int nb = 0; nb < nqb; ++nb)
       dkdv_qblock<D, 1, kPin>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
     if constexpr (kPin) agpr_results_ready();
-    dkdv_store<D, 1>(a, b, h, seq_span(a, b, h), kb_ * KB + 32 * w, dk, dv, lane);
+    dkdv_store<D, 1>(a, b, h, seq_span(a, b, h), kb_ * KB + 32 * w, dk, dv, stage, lane);
   };
   load_kv(kb, kreg, vreg);
   for (; kb + groups < nkb; kb += groups) {
