@@ -227,21 +227,15 @@ __device__ __forceinline__ void negate_rows(bf16x8 (&v)[NCB][KC]) {
 // dK and dV of a wave's keys kw .. kw + 32 NCB - 1 from the transposed
 // accumulators (dk holds -dK / scale, see dkdv_qblock).  A lane owns key
 // kw + 32cb + ln and, per 32-column block db, the runs d = 32db + 8i + 4g +
-// (0..3) (accumulator entries 4i .. 4i+3).  Stored from there, every wave
-// store instruction would touch 32 rows with 16 bytes each, one L2 request
-// per 16 bytes; instead the runs go to this wave's LDS staging rows
-// (`stage`, 32 NCB rows of stride DP + 8) and whole rows are read back and
-// leave in 16-byte stores, so each instruction writes contiguous row memory.
-// The staging rows are this wave's alone and LDS operations of one wave
-// complete in order, so no barrier is needed.
+// (0..3) (accumulator entries 4i .. 4i+3); the runs go through this wave's
+// LDS staging rows (`stage`, 32 NCB rows of stride DP + 8) and leave as
+// whole rows (store_staged_rows).
 template <int D, int NCB>
 __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, const SeqSpan& sp,
                                            int kw, const f32x16 (&dk)[NCB][(D + 31) / 32],
                                            const f32x16 (&dv)[NCB][(D + 31) / 32], bf16* stage,
                                            int lane) {
-  constexpr int NDB = (D + 31) / 32, SRS = NDB * 32 + 8, PPR = D / 8;
-  constexpr int NP = 32 * NCB * PPR / 64;  // 16-byte pieces per lane and tensor
-  static_assert(32 * NCB * PPR % 64 == 0, "whole wave instructions");
+  constexpr int NDB = (D + 31) / 32, SRS = NDB * 32 + 8;
   const int ln = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {  // dK, then dV
@@ -266,11 +260,9 @@ __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, const
                              (int64_t)(sp.kv_row0 + kw) * a.dvs.sn;
     const int64_t sn = t == 0 ? a.dks.sn : a.dvs.sn;
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int e = 64 * j + lane, r = e / PPR, pc = e % PPR;
-      const bf16x8 v = load_bf16x8(&stage[r * SRS + 8 * pc]);
-      if (kw + r < sp.nkv) *reinterpret_cast<bf16x8*>(out + (int64_t)r * sn + 8 * pc) = v;
-    }
+    for (int cb = 0; cb < NCB; ++cb)
+      store_staged_rows<bf16, D, SRS>(stage + 32 * cb * SRS, out + (int64_t)32 * cb * sn, sn,
+                                      sp.nkv - kw - 32 * cb, lane);
   }
 }
 

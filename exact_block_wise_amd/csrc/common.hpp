@@ -220,6 +220,27 @@ struct LdsTileDma {
   }
 };
 
+// Output rows staged in LDS, written out whole.  Kernels whose accumulator
+// layout gives a lane one output row and runs of a few columns would make
+// every wave store instruction touch 32 rows with 8-16 bytes each (one L2
+// request per piece); they write the runs to a wave-private LDS tile first
+// and this copies rows [0, rows) of that tile (row stride SRS elements of T,
+// D columns) to `out` (rows `sn` elements apart) in 16-byte pieces, so each
+// instruction covers contiguous row memory.  A wave's LDS operations
+// complete in order, so the tile needs no barrier when only its wave uses it.
+template <typename T, int D, int SRS>
+__device__ __forceinline__ void store_staged_rows(const T* stage, T* out, int64_t sn, int rows,
+                                                  int lane) {
+  constexpr int PER = 16 / (int)sizeof(T), PPR = D / PER, NP = 32 * PPR / 64;
+  static_assert(D % PER == 0 && 32 * PPR % 64 == 0, "whole 16-byte pieces, whole instructions");
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int e = 64 * j + lane, r = e / PPR, pc = e % PPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[r * SRS + PER * pc]);
+    if (r < rows) *reinterpret_cast<u32x4*>(out + (int64_t)r * sn + PER * pc) = v;
+  }
+}
+
 // The hardware dispatches workgroup i of a launch to XCD i % 8.  Renumber
 // so that each XCD runs a contiguous range of logical workgroups: logical
 // neighbours (tiles of one head) then share that XCD's L2.

@@ -258,14 +258,19 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 
   if (!wave_active) return;
+  // O leaves through this wave's rows of the (now free) key/value tiles:
+  // a lane owns one query row and runs of 4 d of it, which go to LDS first
+  // and then out as whole rows (store_staged_rows); the last tile's barrier
+  // has retired every read of the tiles
+  using OT = std::conditional_t<OUT_F32, float, bf16>;
+  constexpr int SRS = OUT_F32 ? D + 4 : DP + 8;  // staging row stride (16-byte rows)
+  static_assert(4 * 32 * SRS * sizeof(OT) <= sizeof(lds), "staging fits the tiles");
+  OT* const stage = reinterpret_cast<OT*>(lds) + w * 32 * SRS;
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const float l = sum_halves(lsum[qb]);
     const int qrow = q0 + 32 * qb + ln;
-    if (qrow >= sp.nq) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t orow = (int64_t)c * a.o_chunk_stride + b * a.os.sb + h * a.os.sh +
-                         (int64_t)(sp.q_row0 + qrow) * a.os.sn;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -274,18 +279,22 @@ void fwd_bf16_kernel(FwdArgs a) {
         if (d0 < D) {
           const f32x16& o = oacc[db][qb];
           if constexpr (OUT_F32) {
-            f32x4 v4 = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv,
-                        o[4 * i + 3] * inv};
-            *reinterpret_cast<f32x4*>((float*)a.o + orow + d0) = v4;
+            const f32x4 v4 = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv,
+                              o[4 * i + 3] * inv};
+            *reinterpret_cast<f32x4*>(&stage[ln * SRS + d0]) = v4;
           } else {
-            bf16x4 v4 = {(bf16)(o[4 * i] * inv), (bf16)(o[4 * i + 1] * inv),
-                         (bf16)(o[4 * i + 2] * inv), (bf16)(o[4 * i + 3] * inv)};
-            *reinterpret_cast<bf16x4*>((bf16*)a.o + orow + d0) = v4;
+            const bf16x4 v4 = {(bf16)(o[4 * i] * inv), (bf16)(o[4 * i + 1] * inv),
+                               (bf16)(o[4 * i + 2] * inv), (bf16)(o[4 * i + 3] * inv)};
+            *reinterpret_cast<bf16x4*>(&stage[ln * SRS + d0]) = v4;
           }
         }
       }
     }
-    if (g == 0) {
+    const int r0 = q0 + 32 * qb;
+    OT* const out = reinterpret_cast<OT*>(a.o) + (int64_t)c * a.o_chunk_stride + b * a.os.sb +
+                    h * a.os.sh + (int64_t)(sp.q_row0 + r0) * a.os.sn;
+    store_staged_rows<OT, D, SRS>(stage, out, a.os.sn, sp.nq - r0, lane);
+    if (g == 0 && qrow < sp.nq) {
       const int64_t li = (int64_t)c * a.lse_chunk_stride + sp.stat0 + qrow;
       a.lse[li] = l > 0.f ? (mref[qb] * sl2 + log2f(l)) * kLn2 : -INFINITY;
     }
