@@ -241,6 +241,24 @@ __device__ __forceinline__ void store_staged_rows(const T* stage, T* out, int64_
   }
 }
 
+// The same for tiles whose rows are not evenly spaced in memory (rows of
+// different sequences and heads): row r of the staging tile goes to
+// out + offs[r] (elements), or nowhere when offs[r] < 0.  `offs` is LDS the
+// wave filled before the call.
+template <typename T, int D, int SRS>
+__device__ __forceinline__ void store_staged_rows_at(const T* stage, T* out,
+                                                     const int64_t* offs, int lane) {
+  constexpr int PER = 16 / (int)sizeof(T), PPR = D / PER, NP = 32 * PPR / 64;
+  static_assert(D % PER == 0 && 32 * PPR % 64 == 0, "whole 16-byte pieces, whole instructions");
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int e = 64 * j + lane, r = e / PPR, pc = e % PPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[r * SRS + PER * pc]);
+    const int64_t off = offs[r];
+    if (off >= 0) *reinterpret_cast<u32x4*>(out + off + PER * pc) = v;
+  }
+}
+
 // The hardware dispatches workgroup i of a launch to XCD i % 8.  Renumber
 // so that each XCD runs a contiguous range of logical workgroups: logical
 // neighbours (tiles of one head) then share that XCD's L2.

@@ -97,6 +97,7 @@ void fwd_short_kernel(FwdArgs a) {
   constexpr int KC = Dm::KC, NDB = Dm::NDB, RS = Dm::RS;
   constexpr int P = shortk::ROWS / S;
   __shared__ __attribute__((aligned(16))) bf16 vt[Dm::tile];
+  __shared__ int64_t roff[shortk::ROWS];  // output row offsets (staged stores)
   const int lane = threadIdx.x, ln = lane & 31, g = lane >> 5;
   const ShortRow<S> row(a, (int)blockIdx.x * P, ln);  // this lane's query and key row
 
@@ -146,25 +147,37 @@ void fwd_short_kernel(FwdArgs a) {
     }
   }
 
-  if (!rq) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;  // l >= 1 when the query has keys
-  const int64_t orow = row.q_off(a.os);
+  if constexpr (OUT_F32) {
+    if (!rq) return;
+    const int64_t orow = row.q_off(a.os);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = 32 * db + 8 * i + 4 * g;
-      if (d0 >= D) continue;
-      if constexpr (OUT_F32) {
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * g;
+        if (d0 >= D) continue;
         const f32x4 v4 = {o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
                           o[db][4 * i + 3] * inv};
         *reinterpret_cast<f32x4*>((float*)a.o + orow + d0) = v4;
-      } else {
+      }
+  } else {
+    // a lane holds runs of 4 d of its query row: through the V tile (its
+    // transpose reads are done) and out as whole rows
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * g;
+        if (d0 >= D) continue;
         const bf16x4 v4 = {(bf16)(o[db][4 * i] * inv), (bf16)(o[db][4 * i + 1] * inv),
                            (bf16)(o[db][4 * i + 2] * inv), (bf16)(o[db][4 * i + 3] * inv)};
-        *reinterpret_cast<bf16x4*>((bf16*)a.o + orow + d0) = v4;
+        *reinterpret_cast<bf16x4*>(&vt[ln * RS + d0]) = v4;
       }
-    }
+    if (g == 0) roff[ln] = rq ? row.q_off(a.os) : -1;
+    store_staged_rows_at<bf16, D, RS>(vt, (bf16*)a.o, roff, lane);
+    if (!rq) return;
+  }
   if (g == 0) a.lse[row.stat()] = l > 0.f ? m * a.scale + logf(l) : -INFINITY;
 }
 
@@ -196,6 +209,7 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
   bf16* const dOs = KQs + TL;
   float* const lse2s = reinterpret_cast<float*>(dOs + TL);
   float* const Dss = lse2s + shortk::ROWS;
+  __shared__ int64_t roff[shortk::ROWS];  // output row offsets (staged stores)
 
   const int lane = threadIdx.x, ln = lane & 31, g = lane >> 5;
   const ShortRow<S> row(a, (int)blockIdx.x * P, ln);  // this lane's query and key row
@@ -281,24 +295,37 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
         dq[db] = mfma32(kt, sb, dq[db]);
       }
     }
-    if (rq) {
-      const int64_t qrow = row.q_off(a.dqs);
+    if (accumulate) {
+      if (rq) {
+        const int64_t qrow = row.q_off(a.dqs);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * g;
+            if (d0 >= D) continue;
+            f32x4 v4 = {dq[db][4 * i], dq[db][4 * i + 1], dq[db][4 * i + 2], dq[db][4 * i + 3]};
+            v4 *= a.scale;
+            f32x4* p = reinterpret_cast<f32x4*>((float*)a.dq + qrow + d0);
+            *p = *p + v4;
+          }
+      }
+    } else {
+      // runs of 4 d of the lane's query row, through the K tile (its
+      // transpose reads are done; Q replaces it afterwards) and out as rows
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d0 = 32 * db + 8 * i + 4 * g;
           if (d0 >= D) continue;
-          f32x4 v4 = {dq[db][4 * i], dq[db][4 * i + 1], dq[db][4 * i + 2], dq[db][4 * i + 3]};
-          v4 *= a.scale;
-          if (accumulate) {
-            f32x4* p = reinterpret_cast<f32x4*>((float*)a.dq + qrow + d0);
-            *p = *p + v4;
-          } else {
-            const bf16x4 b4 = {(bf16)v4[0], (bf16)v4[1], (bf16)v4[2], (bf16)v4[3]};
-            *reinterpret_cast<bf16x4*>((bf16*)a.dq + qrow + d0) = b4;
-          }
+          const bf16x4 b4 = {(bf16)(dq[db][4 * i] * a.scale), (bf16)(dq[db][4 * i + 1] * a.scale),
+                             (bf16)(dq[db][4 * i + 2] * a.scale),
+                             (bf16)(dq[db][4 * i + 3] * a.scale)};
+          *reinterpret_cast<bf16x4*>(&KQs[ln * RS + d0]) = b4;
         }
+      if (g == 0) roff[ln] = rq ? row.q_off(a.dqs) : -1;
+      store_staged_rows_at<bf16, D, RS>(KQs, (bf16*)a.dq, roff, lane);
     }
   }
 
@@ -346,23 +373,26 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
         dk[db] = mfma32(qt, sb, dk[db]);
       }
     }
-    if (rk) {
-      const int64_t krow = row.kv_off(a.dks), vrow = row.kv_off(a.dvs);
+    // runs of 4 d of the lane's key row, through the Q and dO tiles (their
+    // transpose reads are done) and out as whole rows
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = 32 * db + 8 * i + 4 * g;
-          if (d0 >= D) continue;
-          const bf16x4 k4 = {(bf16)(dk[db][4 * i] * a.scale), (bf16)(dk[db][4 * i + 1] * a.scale),
-                             (bf16)(dk[db][4 * i + 2] * a.scale),
-                             (bf16)(dk[db][4 * i + 3] * a.scale)};
-          const bf16x4 v4 = {(bf16)dv[db][4 * i], (bf16)dv[db][4 * i + 1],
-                             (bf16)dv[db][4 * i + 2], (bf16)dv[db][4 * i + 3]};
-          *reinterpret_cast<bf16x4*>((bf16*)a.dk + krow + d0) = k4;
-          *reinterpret_cast<bf16x4*>((bf16*)a.dv + vrow + d0) = v4;
-        }
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * g;
+        if (d0 >= D) continue;
+        const bf16x4 k4 = {(bf16)(dk[db][4 * i] * a.scale), (bf16)(dk[db][4 * i + 1] * a.scale),
+                           (bf16)(dk[db][4 * i + 2] * a.scale),
+                           (bf16)(dk[db][4 * i + 3] * a.scale)};
+        const bf16x4 v4 = {(bf16)dv[db][4 * i], (bf16)dv[db][4 * i + 1],
+                           (bf16)dv[db][4 * i + 2], (bf16)dv[db][4 * i + 3]};
+        *reinterpret_cast<bf16x4*>(&KQs[ln * RS + d0]) = k4;
+        *reinterpret_cast<bf16x4*>(&dOs[ln * RS + d0]) = v4;
+      }
+    if (g == 0) roff[ln] = rk ? row.kv_off(a.dks) : -1;
+    store_staged_rows_at<bf16, D, RS>(KQs, (bf16*)a.dk, roff, lane);
+    if (g == 0) roff[ln] = rk ? row.kv_off(a.dvs) : -1;
+    store_staged_rows_at<bf16, D, RS>(dOs, (bf16*)a.dv, roff, lane);
   }
 }
 
