@@ -673,6 +673,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   // At d = 80 the 16 registers of D do not fit three waves per SIMD; there
   // D is added per score instead.
   constexpr bool kFoldD = D != 80;
+  constexpr bool kRowOut = D != 80;  // orientation of the dQ accumulators (below)
   f32x16 dinit[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -752,8 +753,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
             const float p = fast_exp2(fmaf(st[cb][qb][e], sl2, -lse2[qb]));
             st[cb][qb][e] = p * (kFoldD ? dpt[cb][qb][e] : dpt[cb][qb][e] + dsum[qb]);
           }
-      // -dQ += (-dS) K over four 16-key chunks (slot group g: keys 16t + 4g +
-      // (0..3) and 16t + 8 + 4g + (0..3) = accumulator entries 8hh..8hh+7)
+      // (-dQ)^T += K^T (-dS)^T over four 16-key chunks (slot group g: keys
+      // 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3) = accumulator entries
+      // 8hh..8hh+7): the K columns (transpose reads) are the A operand, so a
+      // lane's accumulator holds its query row's runs of 4 consecutive d.
+      // At d = 80 that orientation costs spills at three waves per SIMD;
+      // there the product is -dQ += (-dS) K and a lane holds one d column.
       prio_mfma();
 #pragma unroll
       for (int t = 0; t < 2 * NCB; ++t) {
@@ -764,7 +769,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
         for (int db = 0; db < NDB; ++db) {
           const bf16x8 kb8 = tr_operand(Kt + 32 * db, KS, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) dq[qb][db] = mfma32(sa[qb], kb8, dq[qb][db]);
+          for (int qb = 0; qb < NQB; ++qb)
+            dq[qb][db] = kRowOut ? mfma32(kb8, sa[qb], dq[qb][db]) : mfma32(sa[qb], kb8, dq[qb][db]);
         }
       }
       prio_valu();
@@ -788,31 +794,88 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   }
 
   if (!wave_active) return;
-  // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block
+  const float sc = -a.scale;
+  if constexpr (!kRowOut) {
+    // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int dcol = 32 * db + ln;
-      if (dcol >= D) continue;
+      for (int db = 0; db < NDB; ++db) {
+        const int dcol = 32 * db + ln;
+        if (dcol >= D) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (qr >= sp.nq) continue;
-        const float v = dq[qb][db][e] * -a.scale;
-        if (a.dq_splits > 1) {  // this key range's share, summed by dq_reduce_kernel
-          a.dq_part[((((int64_t)split * a.B + b) * a.H + h) * a.Nq + qr) * D + dcol] = v;
-        } else if (accumulate) {
-          float* p = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
-                     (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
-          *p += v;
-        } else {
-          bf16* p = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
-                    (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
-          *p = (bf16)v;
+        for (int e = 0; e < 16; ++e) {
+          const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
+          if (qr >= sp.nq) continue;
+          const float v = dq[qb][db][e] * sc;
+          if (a.dq_splits > 1) {  // this key range's share, summed by dq_reduce_kernel
+            a.dq_part[((((int64_t)split * a.B + b) * a.H + h) * a.Nq + qr) * D + dcol] = v;
+          } else if (accumulate) {
+            float* p = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
+                       (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
+            *p += v;
+          } else {
+            bf16* p = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
+                      (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
+            *p = (bf16)v;
+          }
         }
       }
+    return;
+  }
+  // lane owns query row q0 + 32qb + ln and, per 32-column block db, the runs
+  // d = 32db + 8i + 4g + (0..3) (accumulator entries 4i .. 4i+3)
+  if (a.dq_splits > 1 || accumulate) {
+    // fp32: 16-byte pieces straight from the runs (a key range's share for
+    // dq_reduce_kernel, or added to an fp32 dQ)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qr = q0 + 32 * qb + ln;
+      if (qr >= sp.nq) continue;
+      float* const row =
+          a.dq_splits > 1
+              ? a.dq_part + (((int64_t)split * a.B + b) * a.H + h) * a.Nq * D + (int64_t)qr * D
+              : (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)(sp.q_row0 + qr) * a.dqs.sn;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = 32 * db + 8 * i + 4 * g;
+          if (d0 >= D) continue;
+          const f32x16& x = dq[qb][db];
+          const f32x4 v4 = {x[4 * i] * sc, x[4 * i + 1] * sc, x[4 * i + 2] * sc, x[4 * i + 3] * sc};
+          f32x4* const p = reinterpret_cast<f32x4*>(row + d0);
+          if (a.dq_splits > 1)
+            *p = v4;
+          else
+            *p = *p + v4;
+        }
     }
+    return;
+  }
+  // bf16: the runs go through this wave's rows of the (now free) key/value
+  // tiles and leave as whole rows; the last tile's barrier has retired every
+  // read of the tiles
+  constexpr int SRS = DP + 8;
+  static_assert(4 * 32 * SRS <= 4 * L::tile, "staging fits the tiles");
+  bf16* const stage = lds + w * 32 * SRS;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * g;
+        if (d0 >= D) continue;
+        const f32x16& x = dq[qb][db];
+        const bf16x4 v4 = {(bf16)(x[4 * i] * sc), (bf16)(x[4 * i + 1] * sc),
+                           (bf16)(x[4 * i + 2] * sc), (bf16)(x[4 * i + 3] * sc)};
+        *reinterpret_cast<bf16x4*>(&stage[ln * SRS + d0]) = v4;
+      }
+    const int r0 = q0 + 32 * qb;
+    bf16* const out = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)(sp.q_row0 + r0) * a.dqs.sn;
+    store_staged_rows<bf16, D, SRS>(stage, out, a.dqs.sn, sp.nq - r0, lane);
+  }
 }
 
 // --------------------------------------------------------------------------
