@@ -344,3 +344,40 @@ def test_fp32_bwd_flags():
     torch.cuda.synchronize()
     for a_, b_ in zip(full, (dq, dk, dv)):
         assert torch.equal(a_, b_)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(2, 3, 150, 260, 64), (1, 2, 70, 90, 80),
+                                         (1, 2, 40, 1100, 128), (3, 2, 8, 6, 64)])
+def test_strided_outputs(B, H, Nq, Nkv, d):
+    """O, dQ, dK and dV written into column windows of wider rows (row stride
+    d + 24, 8 guard columns on each side): every output path (whole rows
+    staged through LDS in the general, resident and short-tile kernels; the
+    fp32 dQ accumulation) honours the row stride and writes nothing outside
+    its window."""
+    _say(f"strided outputs {B}x{H}x{Nq}x{Nkv}x{d}")
+    x = synth.random_case(3100 + d + Nq, B, H, Nq, Nkv, d, "bf16")
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    guard = 7.0
+
+    def window(rows, dtype=torch.bfloat16):
+        buf = torch.full((B, H, rows, d + 24), guard, dtype=dtype, device="cuda")
+        return buf, buf[:, :, :, 8:8 + d]
+
+    ob, o = window(Nq)
+    dqb, dq = window(Nq)
+    dkb, dk = window(Nkv)
+    dvb, dv = window(Nkv)
+    accb, acc = window(Nq, torch.float32)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    ebw.fwd(q, k, v, scale=scale, out=o, lse=lse)
+    ebw.bwd(q, k, v, o, do, lse, scale=scale, dq=dq, dk=dk, dv=dv)
+    ebw.bwd(q, k, v, o, do, lse, scale=scale, dq=acc, accumulate_dq=True, need_dkdv=False)
+    torch.cuda.synchronize()
+    for buf in (ob, dqb, dkb, dvb, accb):
+        assert bool((buf[..., :8] == guard).all()) and bool((buf[..., 8 + d:] == guard).all())
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], scale)
+    check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16")
+    ref = oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale)
+    check_grads([to_host(t) for t in (dq, dk, dv)], ref, "bf16", "strided outputs")
+    check_grads([to_host(acc) - guard, ref[1], ref[2]], ref, "bf16", "strided accumulation")
