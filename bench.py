@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="time only plain bf16 GEMMs through the vendor library (torch.matmul / "
                          "hipBLASLt): the matrix-core rate this GPU sustains outside attention")
+    ap.add_argument("--make-mfma-profile", metavar="PMC_DIR",
+                    help="turn a rocprofv3 --pmc run with the matrix-core counters (see "
+                         "MFMA_COUNTERS) into profiles/*_mfma_utilisation.txt (workload "
+                         "gemm_ceiling: a run of --gemm-ceiling)")
     ap.add_argument("--make-traffic-profile", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
                     "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results of a bench run "
@@ -183,6 +187,85 @@ def make_traffic_profile(dirs, workload):
     print(open(out).read())
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+
+
+def make_mfma_profile(d, workload):
+    """Matrix-core utilisation per kernel from one rocprofv3 run with
+    --pmc MFMA_COUNTERS: busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) /
+    (GRBM_GUI_ACTIVE per XCD x SIMD count); executed matrix flops =
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; shader clock while the kernel runs =
+    GRBM_GUI_ACTIVE per XCD / the dispatch's duration."""
+    gemm = workload == "gemm_ceiling"  # the run of --gemm-ceiling
+    w = None if gemm else find_workload(workload)
+    agent = [r for f in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True)
+             for r in csv.DictReader(open(f)) if r.get("Name", "").startswith("gfx")][0]
+    simds, cus, fmax = int(agent["Simd_Count"]), int(agent["Cu_Count"]), int(
+        agent["Max_Engine_Clk_Fcompute"])
+    xcds = int(agent.get("Num_Xcc") or 1)
+    dur = {}
+    acc = {}  # (dir, dispatch) -> counter -> value (rocprofv3 sums the instances)
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            key = (f.rsplit("/", 1)[0], r["Dispatch_Id"])
+            acc.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            dur[key] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    units = 0 if gemm else (w.B * w.H * w.Nq * w.Nkv * w.d if not is_packed(w) else sum(
+        n * n for n in w.lens) * w.H * w.d)
+    credit = {"fwd_": 4.0, "dq_bf16_kernel": 6.0, "dkdv_": 8.0}
+    rows = {}
+    for key, cs in acc.items():
+        if key not in dur or "GRBM_GUI_ACTIVE" not in cs:
+            continue
+        name, ns = dur[key]
+        if "Cijk" in name:  # the vendor GEMM of --gemm-ceiling: tagged by its shape
+            name = "hipBLASLt GEMM (" + name[:40] + "...)"
+        elif not any(s_ in name for s_ in credit):
+            continue
+        # GRBM_GUI_ACTIVE comes summed over the XCDs: the shader clock counts
+        # of one XCD are that over the XCD count
+        busy, grbm = cs["SQ_VALU_MFMA_BUSY_CYCLES"], cs["GRBM_GUI_ACTIVE"] / xcds
+        mops = cs["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        if name.startswith("hipBLASLt"):
+            n_ = round((mops * 512 / 2) ** (1 / 3))  # square n x n x n
+            name = f"hipBLASLt bf16 GEMM n={n_}"
+        rows.setdefault(name, []).append((busy / (grbm * simds), mops * 512, grbm / ns, ns))
+    stem = "bf16_gemm_ceiling" if gemm else workload
+    run = "--gemm-ceiling" if gemm else f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline"
+    out = os.path.join(ROOT, "profiles", f"{stem}_mfma_utilisation.txt")
+    with open(out, "w") as f:
+        f.write(f"# matrix-core utilisation per kernel, {'the vendor GEMMs of --gemm-ceiling' if gemm else 'workload ' + workload}, from rocprofv3 --pmc\n")
+        f.write("# command (repo root, MI355X):\n")
+        f.write(f"#   rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv -d <D> "
+                f"-- python bench.py {run}\n")
+        f.write(f"#   python bench.py --workload {workload} --make-mfma-profile <D>\n")
+        f.write(f"# device (rocprofv3 agent info): {agent['Name']}, {cus} CUs, {simds} SIMDs, "
+                f"max shader clock {fmax} MHz\n")
+        f.write(f"# GRBM_GUI_ACTIVE as written is summed over the {xcds} XCDs; per XCD = value / "
+                f"{xcds}.\n")
+        f.write("# busy = SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) / (GRBM_GUI_ACTIVE per XCD x SIMDs);\n")
+        f.write("# clock = GRBM_GUI_ACTIVE per XCD / duration (the dispatch's timestamps);\n")
+        f.write("# executed flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (padding included: at d = 80\n"
+                "# the products run on 96 columns); design = the flops of the kernel's products at\n"
+                "# the true d (forward 4u, dQ 6u with its S and dP recomputation, dK/dV 8u, where\n"
+                "# u = B*H*Nq*Nkv*d; the bench line credits dQ with 2u only).\n")
+        f.write("# Means over the run's dispatches; counter collection serialises kernels, so the\n"
+                "# durations are not the bench's.  peak@clock = 2.5 PFLOP/s x clock / max clock.\n")
+        f.write(f"{'kernel':58s} {'disp':>4s} {'busy':>6s} {'clock_MHz':>9s} {'exec_GF':>8s} "
+                f"{'design_GF':>9s} {'exec_TF/s':>9s} {'peak@clock':>10s}\n")
+        for name, rs in sorted(rows.items()):
+            n = len(rs)
+            busy = sum(r[0] for r in rs) / n
+            fl = sum(r[1] for r in rs) / n
+            clk = sum(r[2] for r in rs) / n * 1e3
+            ns = sum(r[3] for r in rs) / n
+            cred = next((credit[s_] * units / 1e9 for s_ in credit if s_ in name), None)
+            cred_s = f"{cred:9.1f}" if cred is not None else f"{'-':>9s}"
+            f.write(f"{name[:58]:58s} {n:4d} {busy:6.3f} {clk:9.0f} {fl / 1e9:8.1f} "
+                    f"{cred_s} {fl / ns / 1e3:9.1f} {PEAK_BF16_TFLOPS * clk / fmax:10.1f}\n")
+    print(open(out).read())
+
+
 def measured_traffic(call, workload, short=False):
     """traffic_bytes of `call` from profiles/, or None if absent or stale."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
@@ -263,6 +346,9 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.make_mfma_profile:
+        make_mfma_profile(args.make_mfma_profile, args.workload)
+        return
     if args.make_traffic_profile:
         make_traffic_profile(args.make_traffic_profile, args.workload)
         return
