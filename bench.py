@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="vit_b")
+    ap.add_argument("--workload", default=None,
+                    help="one workload only (default: the ViT-B headline line, with every "
+                         "other workload summarised under other_workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -344,29 +346,12 @@ def cpu_baseline(w, budget_s):
                       f" of {w.name}, fwd+bwd in fp64 NumPy, {t_work:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.make_mfma_profile:
-        make_mfma_profile(args.make_mfma_profile, args.workload)
-        return
-    if args.make_traffic_profile:
-        make_traffic_profile(args.make_traffic_profile, args.workload)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gemm_ceiling:
-        gemm_ceiling()
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(--gpus must be 1)", file=sys.stderr)
-        sys.exit(2)
+def run_workload(w, steps, warmup):
+    """Time `steps` steps of workload w (after `warmup` untimed ones) and
+    return its bench line (without the CPU baseline)."""
     import torch
     import exact_block_wise_amd as ebw
     from exact_block_wise_amd import synth
-
-    w = find_workload(args.workload)
     packed = is_packed(w)
     dev = upload(w, torch)
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
@@ -425,12 +410,12 @@ def main():
             q, k, v, None, do, lse, scale=w.scale, dk=dk, dv=dv, workspace=ws,
             d_precomputed=True, need_dq=False)))
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         for c in calls:
             c[3]()
     torch.cuda.synchronize()
 
-    K = args.steps
+    K = steps
     n = len(calls)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(K)]
     torch.cuda.synchronize()
@@ -505,7 +490,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "step_ms_stats": step_stats,
         "higher_is_better": True,
@@ -525,8 +510,58 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    return line
+
+
+# every workload of the default run, the headline first
+ALL_WORKLOADS = ["vit_b", "vit_l", "vit_h14", "xattn", "vit_b_temporal", "vit_b_spatial",
+                 "vit_b_packed", "tiny_f32"]
+
+
+def summary(line):
+    r = line["roofline"]
+    return {"value": line["value"], "unit": line["unit"], "pct_of_peak": line["pct_of_peak"],
+            "ms_per_step": line["ms_per_step"], "dtype": line["dtype"], "config": line["config"],
+            "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac")}}
+
+
+def main():
+    args = parse()
+    if args.make_mfma_profile:
+        make_mfma_profile(args.make_mfma_profile, args.workload or ALL_WORKLOADS[0])
+        return
+    if args.make_traffic_profile:
+        make_traffic_profile(args.make_traffic_profile, args.workload or ALL_WORKLOADS[0])
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling()
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import exact_block_wise_amd as ebw
+    ebw.load()  # fails loudly without the built library
+
+    w = find_workload(args.workload or ALL_WORKLOADS[0])
+    line = run_workload(w, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if args.workload is None:
+        # the default run also measures every other workload (20 steps each),
+        # each summarised in one entry; a failure there is reported, not fatal
+        others = {}
+        for name in ALL_WORKLOADS[1:]:
+            try:
+                others[name] = summary(run_workload(find_workload(name), 20, 5))
+            except Exception as e:  # noqa: BLE001 - reported in the line
+                others[name] = {"error": f"{type(e).__name__}: {e}"[:300]}
+            torch.cuda.empty_cache()
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
 
