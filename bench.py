@@ -521,7 +521,9 @@ ALL_WORKLOADS = ["vit_b", "vit_l", "vit_h14", "xattn", "vit_b_temporal", "vit_b_
 def summary(line):
     r = line["roofline"]
     return {"value": line["value"], "unit": line["unit"], "pct_of_peak": line["pct_of_peak"],
-            "ms_per_step": line["ms_per_step"], "dtype": line["dtype"], "config": line["config"],
+            "ms_per_step": line["ms_per_step"], "step_ms_stats": line["step_ms_stats"],
+            "steps": line["steps"], "warmup": line["warmup"], "dtype": line["dtype"],
+            "config": line["config"],
             "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac")}}
 
 
@@ -556,8 +558,10 @@ def main():
         # each summarised in one entry; a failure there is reported, not fatal
         others = {}
         for name in ALL_WORKLOADS[1:]:
+            # the latency-bound fp32 case gets more repetitions (50 warm-up, 200 timed)
+            steps, warm = (200, 50) if name == "tiny_f32" else (20, 5)
             try:
-                others[name] = summary(run_workload(find_workload(name), 20, 5))
+                others[name] = summary(run_workload(find_workload(name), steps, warm))
             except Exception as e:  # noqa: BLE001 - reported in the line
                 others[name] = {"error": f"{type(e).__name__}: {e}"[:300]}
             torch.cuda.empty_cache()
