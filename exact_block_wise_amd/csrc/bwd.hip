@@ -1009,52 +1009,80 @@ __global__ __launch_bounds__((64 * bwdf::waves<D, true>())) void bwd_f32_dkdv_ke
     Kown[r][cc] = ok ? kp[(int64_t)(k0 + r) * a.ks.sn + cc] : 0.f;
     Vown[r][cc] = ok ? vp[(int64_t)(k0 + r) * a.vs.sn + cc] : 0.f;
   }
-  float dk[D], dv[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) dk[i] = dv[i] = 0.f;
-  for (int q0 = 0; q0 < a.Nq; q0 += BS) {
-    __syncthreads();
-    for (int e = tid; e < BS * D; e += 64 * W) {
-      const int r = e / D, cc = e % D;
-      const bool ok = q0 + r < a.Nq;
-      Qt[r][cc] = ok ? qp[(int64_t)(q0 + r) * a.qs.sn + cc] : 0.f;
-      dOt[r][cc] = ok ? dop[(int64_t)(q0 + r) * a.dos.sn + cc] : 0.f;
-    }
-    if (tid < BS) {
-      const bool ok = q0 + tid < a.Nq;
-      lse_t[tid] = ok ? lsep[q0 + tid] : INFINITY;
-      D_t[tid] = ok ? dsp[q0 + tid] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int t = 0; t < TB; ++t) {
-      const int j = w * TB + t;  // rows past Nq: Q = dO = 0, LSE = +inf, so P = 0
-      float s4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < D; ++i) {
-        s4[i & 3] = fmaf(Qt[j][i], Kown[lane][i], s4[i & 3]);
-        p4[i & 3] = fmaf(dOt[j][i], Vown[lane][i], p4[i & 3]);
-      }
-      const float sv = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      const float dpv = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-      const float p = expf(sv * a.scale - lse_t[j]);
-      const float ds = p * (dpv - D_t[j]);
-#pragma unroll
-      for (int i = 0; i < D; ++i) {
-        dv[i] = fmaf(p, dOt[j][i], dv[i]);
-        dk[i] = fmaf(ds, Qt[j][i], dk[i]);
-      }
-    }
-  }
-  sum_over_waves<W, D>(dk, Ab, w, lane);
-  sum_over_waves<W, D>(dv, Ab, w, lane);
+  // One pass over the query rows accumulates the gradients in GRADS (1: dV,
+  // 2: dK, 3: both).  At d = 128 the two accumulators (256 registers) do not
+  // fit the vector registers a VALU instruction can address, so dV and dK
+  // take a pass each (the scores computed twice) instead of spilling.
   const int kr = k0 + lane;
-  if (w != 0 || kr >= a.Nkv) return;
-  float* dkp = (float*)a.dk + b * a.dks.sb + h * a.dks.sh + (int64_t)kr * a.dks.sn;
-  float* dvp = (float*)a.dv + b * a.dvs.sb + h * a.dvs.sh + (int64_t)kr * a.dvs.sn;
-  for (int i = 0; i < D; ++i) {
-    dkp[i] = dk[i] * a.scale;
-    dvp[i] = dv[i];
+  auto pass = [&](auto grads_tag) {
+    constexpr int GR = decltype(grads_tag)::value;
+    constexpr bool DV = GR & 1, DK = GR & 2;
+    float acc_v[DV ? D : 1], acc_k[DK ? D : 1];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if constexpr (DV) acc_v[i] = 0.f;
+      if constexpr (DK) acc_k[i] = 0.f;
+    }
+    for (int q0 = 0; q0 < a.Nq; q0 += BS) {
+      __syncthreads();
+      for (int e = tid; e < BS * D; e += 64 * W) {
+        const int r = e / D, cc = e % D;
+        const bool ok = q0 + r < a.Nq;
+        Qt[r][cc] = ok ? qp[(int64_t)(q0 + r) * a.qs.sn + cc] : 0.f;
+        dOt[r][cc] = ok ? dop[(int64_t)(q0 + r) * a.dos.sn + cc] : 0.f;
+      }
+      if (tid < BS) {
+        const bool ok = q0 + tid < a.Nq;
+        lse_t[tid] = ok ? lsep[q0 + tid] : INFINITY;
+        D_t[tid] = ok ? dsp[q0 + tid] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int t = 0; t < TB; ++t) {
+        const int j = w * TB + t;  // rows past Nq: Q = dO = 0, LSE = +inf, so P = 0
+        // the lane's own K / V row; at d = 128 it is re-read from LDS per
+        // query row rather than held in registers (that would not fit)
+        const float* krow = Kown[lane];
+        const float* vrow = Vown[lane];
+        if constexpr (D > 80) asm volatile("" : "+v"(krow), "+v"(vrow));
+        float s4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          s4[i & 3] = fmaf(Qt[j][i], krow[i], s4[i & 3]);
+          if constexpr (DK) p4[i & 3] = fmaf(dOt[j][i], vrow[i], p4[i & 3]);
+        }
+        const float sv = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        const float p = expf(sv * a.scale - lse_t[j]);
+        float ds = 0.f;
+        if constexpr (DK) {
+          const float dpv = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+          ds = p * (dpv - D_t[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          if constexpr (DV) acc_v[i] = fmaf(p, dOt[j][i], acc_v[i]);
+          if constexpr (DK) acc_k[i] = fmaf(ds, Qt[j][i], acc_k[i]);
+        }
+      }
+    }
+    if constexpr (DK) sum_over_waves<W, D>(acc_k, Ab, w, lane);
+    if constexpr (DV) sum_over_waves<W, D>(acc_v, Ab, w, lane);
+    if (w == 0 && kr < a.Nkv) {
+      if constexpr (DK) {
+        float* dkp = (float*)a.dk + b * a.dks.sb + h * a.dks.sh + (int64_t)kr * a.dks.sn;
+        for (int i = 0; i < D; ++i) dkp[i] = acc_k[i] * a.scale;
+      }
+      if constexpr (DV) {
+        float* dvp = (float*)a.dv + b * a.dvs.sb + h * a.dvs.sh + (int64_t)kr * a.dvs.sn;
+        for (int i = 0; i < D; ++i) dvp[i] = acc_v[i];
+      }
+    }
+  };
+  if constexpr (D > 80) {
+    pass(std::integral_constant<int, 1>{});
+    pass(std::integral_constant<int, 2>{});
+  } else {
+    pass(std::integral_constant<int, 3>{});
   }
 }
 
