@@ -339,8 +339,18 @@ def cpu_baseline(w, budget_s):
             oracle.head_bwd(x["q"], x["k"], x["v"], x["do"], w.scale)
         t_work += time.perf_counter() - t0
         heads += 1
+    cpu_model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(flops / t_work / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+            "numpy": __import__("numpy").__version__,
             "sample": f"{heads} of {len(order)} heads " +
                       ("(sequence, head)" if is_packed(w) else "(b, h)") +
                       f" of {w.name}, fwd+bwd in fp64 NumPy, {t_work:.1f} s"}
