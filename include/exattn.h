@@ -104,7 +104,8 @@ typedef struct {
  *      natural log, scale included.  Written, never read.
  *
  * The log-sum-exp is the one O(N) statistic the backward needs (weights are
- * recomputed from it, not stored: the page's memory argument, section 4.1)
+ * recomputed from it, not stored: the memory argument of "Training a Large
+ * Video Model on a Single Machine in a Day", section 4.1)
  * and the one that lets partial results over disjoint key sets be merged
  * exactly (attn_lse_merge).
  */
