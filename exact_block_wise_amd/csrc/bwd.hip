@@ -542,11 +542,12 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
 // tiles of 64 rows stream through LDS (row-major, double-buffered).  Per tile
 // each wave recomputes the transposed tiles S^T = K Q^T and dP^T = V dO^T, so
 // every lane owns one query row (its LSE and D are per-lane scalars), forms
-// dS = P (dP - D), and accumulates dQ = dS K in registers: the accumulator
-// halves are the A operand and the K columns come from LDS transpose reads.
-// Each dQ row belongs to one workgroup, so no atomics are needed and the
-// result is bitwise reproducible.  Key rows past Nkv are zero in LDS and add
-// nothing (their K rows multiply dS).
+// dS = P (dP - D), and accumulates dQ in registers from the accumulator
+// halves of dS and the K columns (LDS transpose reads) as (dQ)^T = K^T dS^T,
+// so a lane ends up holding its query row's runs of d (d = 80: dQ = dS K,
+// see below).  Each dQ row belongs to one workgroup, so no atomics are
+// needed and the result is bitwise reproducible.  Key rows past Nkv are zero
+// in LDS and add nothing (their K rows multiply dS).
 // --------------------------------------------------------------------------
 namespace dqk {
 constexpr int BN = 64;
