@@ -88,12 +88,25 @@ def find_workload(name):
     return synth.WORKLOADS[name]
 
 
+def _code_only(text):
+    """Source text without // comments and blank lines (a comment edit does
+    not change the kernel)."""
+    out = []
+    for ln in text.splitlines():
+        code = ln.split("//", 1)[0].rstrip()
+        if code:
+            out.append(code)
+    return "\n".join(out)
+
+
 def source_digest(call, short=False):
+    """Digest of the code (comments excluded) of the source a call's kernels
+    come from, with the shared header."""
     src = "short.hip" if short else KERNEL_SOURCES[call]
     path = os.path.join(ROOT, "exact_block_wise_amd", "csrc", src)
     h = hashlib.sha256()
     for p in (path, os.path.join(ROOT, "exact_block_wise_amd", "csrc", "common.hpp")):
-        h.update(open(p, "rb").read())
+        h.update(_code_only(open(p, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
