@@ -194,8 +194,8 @@ def make_traffic_profile(dirs, workload):
         f.write(f"# copy calibration: {COPY_BYTES} bytes read and written; counter/bytes "
                 f"factors fetch={cf:.4f} write={cw:.4f}\n")
         f.write("# traffic_bytes = fetch_kib*1024/fetch_factor + write_kib*1024/write_factor;\n")
-        f.write("# source = digest of the kernel's source when measured (the bench reports the\n")
-        f.write("# traffic only while the source is unchanged)\n")
+        f.write("# source = digest of the kernel's source code, comments excluded, when measured\n")
+        f.write("# (the bench reports the traffic only while that code is unchanged)\n")
         f.write(f"copy_fetch_factor={cf:.6f} copy_write_factor={cw:.6f}\n")
         for ln in lines:
             f.write(ln + "\n")
