@@ -199,7 +199,10 @@ struct ShortBwdLds {
 };
 
 template <int D, int S>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 80 ? 3 : 2)))
+// occupancy: four waves per SIMD at d = 64 (125 registers, no spills; 5%
+// faster than three on the temporal layer), three at d = 80, two at 128
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D <= 80 ? 3 : 2)))
 void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
   using Dm = ShortDims<D>;
   constexpr int KC = Dm::KC, NDB = Dm::NDB, RS = Dm::RS, TL = Dm::tile;
