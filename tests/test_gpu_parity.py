@@ -381,3 +381,38 @@ def test_strided_outputs(B, H, Nq, Nkv, d):
     ref = oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale)
     check_grads([to_host(t) for t in (dq, dk, dv)], ref, "bf16", "strided outputs")
     check_grads([to_host(acc) - guard, ref[1], ref[2]], ref, "bf16", "strided accumulation")
+
+
+@pytest.mark.parametrize("Nq,Nkv,d", [(150, 260, 64), (8, 8, 64), (100, 700, 128)])
+def test_head_offsets_beyond_4gib(Nq, Nkv, d):
+    """Every input and output a view whose second head starts 4 GiB + 4 KiB
+    after its first: each kernel forms a head's address in 64 bits and its
+    32-bit buffer offsets stay within one tile from there.  The three shapes
+    take the general kernels, the short-sequence tiles, and the resident
+    dK/dV kernel with the split dQ."""
+    B, H = 1, 2
+    sh = (1 << 31) + 2048  # bf16 elements between the heads
+    _say(f"head offsets beyond 4 GiB: {B}x{H}x{Nq}x{Nkv}x{d}")
+    x = synth.random_case(4100 + Nq + d, B, H, Nq, Nkv, d, "bf16")
+    scale = float(np.float32(1 / np.sqrt(d)))
+
+    def far(rows, data=None):
+        base = torch.empty(sh + rows * d, dtype=torch.bfloat16, device="cuda")
+        t = base.as_strided((B, H, rows, d), (H * sh, sh, d, 1))
+        if data is not None:
+            t.copy_(to_dev(data, "bf16"))
+        return t
+
+    q, do = far(Nq, x["q"]), far(Nq, x["do"])
+    k, v = far(Nkv, x["k"]), far(Nkv, x["v"])
+    o, dq, dk, dv = far(Nq), far(Nq), far(Nkv), far(Nkv)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    ebw.fwd(q, k, v, scale=scale, out=o, lse=lse)
+    ebw.bwd(q, k, v, o, do, lse, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.ref_fwd(x["q"], x["k"], x["v"], scale)
+    check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "far heads")
+    check_grads([to_host(t) for t in (dq, dk, dv)],
+                oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale), "bf16", "far heads")
+    del q, do, k, v, o, dq, dk, dv
+    torch.cuda.empty_cache()
