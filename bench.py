@@ -111,14 +111,27 @@ def source_digest(call, short=False):
 
 
 def copy_calibration():
-    """A plain copy of COPY_BYTES (read once, written once), repeated."""
+    """A plain copy of COPY_BYTES (read once, written once), repeated; also
+    reports the rate it sustains (bytes read plus written per second, HIP
+    events), the HBM rate a streaming kernel reaches on this GPU in practice
+    next to the published 8 TB/s."""
     import torch
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": COPY_BYTES}))
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes": COPY_BYTES, "ms_per_copy": round(ms, 5),
+                      "copy_GBps": round(2 * COPY_BYTES / ms / 1e6, 1),
+                      "frac_of_8TBps": round(2 * COPY_BYTES / ms / 1e6 / PEAK_HBM_GBS, 3)}))
 
 
 def gemm_ceiling():
