@@ -520,9 +520,19 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
     for (int nb = 0; nb < nqb; ++nb)
       dkdv_qblock<D, 1, kPin>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
     if constexpr (kPin) agpr_results_ready();
+    // The next block's rows were requested a whole block ago: wait for them
+    // here, before this block's stores.  Loads and stores share one counter
+    // and the compiler treats a mix of both as unordered, so a wait for the
+    // rows placed after the stores drains the stores as well, every block.
+    wait_vmem();
     dkdv_store<D, 1>(a, b, h, seq_span(a, b, h), kb_ * KB + 32 * w, dk, dv, stage, lane);
   };
   load_kv(kb, kreg, vreg);
+  // Take the first rows here.  A load still pending on entry would make the
+  // compiler wait at the top of every iteration for whatever was issued
+  // before that iteration's prefetch (the previous block's stores, too).
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) asm volatile("" ::"v"(kreg[0][kc]), "v"(vreg[0][kc]));
   for (; kb + groups < nkb; kb += groups) {
     load_kv(kb + groups, knext, vnext);
     block(kb);
