@@ -245,8 +245,8 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_t
   a.o_f32 = o.dtype == ATTN_F32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!pre_done) {
-    if (do_dq && dt == ATTN_BF16) {
-      a.dq_computes_d = 1;  // the bf16 dQ kernel forms D and runs first
+    if (do_dq && dt == ATTN_BF16 && !a.o_f32) {
+      a.dq_computes_d = 1;  // the bf16 dQ kernel forms D from a bf16 O and runs first
     } else {
       const hipError_t e = launch_bwd_pre(a, p->d, dt == ATTN_BF16, s);
       if (e != hipSuccess) return ATTN_E_HIP;
@@ -329,8 +329,8 @@ attn_status attn_bwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, 
   a.cu_q = p->cu_q; a.cu_kv = p->cu_kv; a.total_q = p->total_q;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!pre_done) {
-    if (do_dq) {
-      a.dq_computes_d = 1;  // the dQ kernel (or the packed-tile kernel) forms D
+    if (do_dq && !a.o_f32) {
+      a.dq_computes_d = 1;  // the dQ kernel (or the packed-tile kernel) forms D from a bf16 O
     } else {
       // D over all packed query tokens: the dense preprocess of one
       // [1, H, total_q, d] problem writes the same [H, total_q] order

@@ -628,55 +628,54 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
       for (int kc = 0; kc < KC; ++kc)
         doreg[qb][kc] = buffer_load_bf16x8(rd, (uint32_t)(r * 2 * a.dos.sn + 2 * (16 * kc + 8 * g)));
     }
-    if (a.dq_computes_d) {
-      // D_i = dO_i . O_i from the stored O (the backward preprocess, done
-      // here on the rows this wave holds, before its Q rows are loaded);
-      // lanes l and l + 32 hold the two halves of each row's d.  Key range 0
-      // writes D for the dK/dV pass.
-      const int ob = a.o_f32 ? 4 : 2;
-      const char* opb =
-          (const char*)a.o + (b * a.os.sb + h * a.os.sh + (int64_t)sp.q_row0 * a.os.sn) * ob;
-      const auto ro = rows_rsrc(opb + (int64_t)q0 * a.os.sn * ob, rows, ob * a.os.sn, ob * D);
+    auto load_q = [&] {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const int r = 32 * qb + ln;
-        float part = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          qreg[qb][kc] = buffer_load_bf16x8(rq, (uint32_t)(r * 2 * a.qs.sn + 2 * (16 * kc + 8 * g)));
+        const float l = buffer_load_f32(rl, 4 * r);
+        lse2[qb] = r < rows ? l * kLog2e : INFINITY;
+      }
+    };
+    // the Q rows and LSE go out with the dO rows (one round trip for all);
+    // at d = 128 only after D, where holding them early costs more than the
+    // round trip (measured)
+    constexpr bool kQFirst = D != 128;
+    if constexpr (kQFirst) load_q();
+    if (a.dq_computes_d) {
+      // D_i = dO_i . O_i from the stored bf16 O (the backward preprocess,
+      // done here on the rows this wave holds);
+      // lanes l and l + 32 hold the two halves of each row's d.  Key range 0
+      // writes D for the dK/dV pass.  (An fp32 O goes through the preprocess
+      // kernel instead: one straight path here lets the O loads go out
+      // together.)
+      const bf16* opb = (const bf16*)a.o + b * a.os.sb + h * a.os.sh + (int64_t)sp.q_row0 * a.os.sn;
+      const auto ro = rows_rsrc(opb + (int64_t)q0 * a.os.sn, rows, 2 * a.os.sn, 2 * D);
+      float part[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int r = 32 * qb + ln;
+        part[qb] = 0.f;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const uint32_t off = (uint32_t)(r * ob * a.os.sn + ob * (16 * kc + 8 * g));
-          float o8[8];
-          if (a.o_f32) {
-            const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
-            const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 16, 0, 0));
+          const bf16x8 v = buffer_load_bf16x8(ro, (uint32_t)(r * 2 * a.os.sn + 2 * (16 * kc + 8 * g)));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              o8[j] = lo[j];
-              o8[4 + j] = hi[j];
-            }
-          } else {
-            const bf16x8 v = buffer_load_bf16x8(ro, off);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o8[j] = (float)v[j];
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) part = fmaf((float)doreg[qb][kc][j], o8[j], part);
+          for (int j = 0; j < 8; ++j) part[qb] = fmaf((float)doreg[qb][kc][j], (float)v[j], part[qb]);
         }
-        dsum[qb] = sum_halves(part);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int r = 32 * qb + ln;
+        dsum[qb] = sum_halves(part[qb]);
         if (split == 0 && g == 0 && r < rows) a.dsum[sp.stat0 + q0 + r] = dsum[qb];
       }
     } else {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) dsum[qb] = buffer_load_f32(rs, 4 * (32 * qb + ln));
     }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int r = 32 * qb + ln;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        qreg[qb][kc] = buffer_load_bf16x8(rq, (uint32_t)(r * 2 * a.qs.sn + 2 * (16 * kc + 8 * g)));
-      const float l = buffer_load_f32(rl, 4 * r);
-      lse2[qb] = r < rows ? l * kLog2e : INFINITY;
-    }
+    if constexpr (!kQFirst) load_q();
   }
   // E^T = D - dP^T: the matrix-core chain of dP^T = V dO^T runs on the
   // negated dO rows and starts from D (every entry of a lane's accumulator

@@ -52,7 +52,7 @@ struct BwdArgs {
   int o_f32;     // o dtype is fp32
   int dq_splits;     // key ranges the dQ pass is split into (1: none)
   int dq_split_len;  // keys per range, a multiple of the key tile
-  int dq_computes_d; // the bf16 dQ kernel forms D from o and dout and writes dsum
+  int dq_computes_d; // the bf16 dQ kernel forms D from a bf16 o and dout and writes dsum
   // packed variable-length sequences, as in FwdArgs (LSE and D [H, total_q])
   const int* cu_q;
   const int* cu_kv;

@@ -231,31 +231,22 @@ void bwd_short_kernel(BwdArgs a, int do_dq, int do_dkdv, int accumulate) {
   const float lse2 = lse_r == -INFINITY ? INFINITY : lse_r * kLog2e;
   float dsum = 0.f;
   if (a.dq_computes_d) {
-    const int ob = a.o_f32 ? 4 : 2;
-    const char* orow = (const char*)a.o + row.q_off(a.os) * ob;
+    // D from the stored bf16 O (an fp32 O goes through the preprocess
+    // kernel): all of the row's pieces are requested under one condition, so
+    // they arrive together
+    bf16x8 ov[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) ov[kc] = bf16x8{};
+    if (rq) {
+      const bf16* orow = (const bf16*)a.o + row.q_off(a.os);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) ov[kc] = load_bf16x8(orow + 16 * kc + 8 * g);
+    }
     float part = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      float o8[8];
-      if (!rq) {
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o8[j] = 0.f;
-      } else if (a.o_f32) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(orow + 4 * (16 * kc + 8 * g));
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(orow + 4 * (16 * kc + 8 * g + 4));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o8[j] = lo[j];
-          o8[4 + j] = hi[j];
-        }
-      } else {
-        const bf16x8 v = load_bf16x8(reinterpret_cast<const bf16*>(orow) + 16 * kc + 8 * g);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o8[j] = (float)v[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) part = fmaf((float)dob[kc][j], o8[j], part);
-    }
+      for (int j = 0; j < 8; ++j) part = fmaf((float)dob[kc][j], (float)ov[kc][j], part);
     dsum = sum_halves(part);
     if (g == 0 && rq) a.dsum[srow] = dsum;
   } else if (rq) {
