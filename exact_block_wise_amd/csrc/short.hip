@@ -56,13 +56,19 @@ struct ShortRow {
 };
 
 // One row per lane as matrix-core operands: lane (l % 32, g = l / 32) holds
-// d = 16 kc + 8 g .. +7 of its row for each kc (zeros when !ok).
+// d = 16 kc + 8 g .. +7 of its row for each kc (zeros when !ok).  The zeros
+// are written first and the loads go out under one condition: a select of
+// each loaded piece would use it at once and make every call wait for its
+// own loads.
 template <int KC>
 __device__ __forceinline__ void load_row_operands(bf16x8 (&dst)[KC], const bf16* row, bool ok,
                                                   int g) {
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    dst[kc] = ok ? load_bf16x8(row + 16 * kc + 8 * g) : bf16x8{};
+  for (int kc = 0; kc < KC; ++kc) dst[kc] = bf16x8{};
+  if (ok) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) dst[kc] = load_bf16x8(row + 16 * kc + 8 * g);
+  }
 }
 
 // The same pieces into a row-major LDS tile (row stride RS), for transpose
