@@ -806,31 +806,62 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   if (!wave_active) return;
   const float sc = -a.scale;
   if constexpr (!kRowOut) {
-    // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block
+    // lane owns column d = 32db + ln, query rows 8i + 4g + r of each block.
+    // The three destinations are chosen outside the unrolled loops, and the
+    // accumulating one reads every value it adds to before its first store
+    // (one round trip instead of one per value).
+    auto each = [&](auto&& f) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int dcol = 32 * db + ln;
-        if (dcol >= D) continue;
+        for (int db = 0; db < NDB; ++db) {
+          const int dcol = 32 * db + ln;
+          if (dcol >= D) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (qr >= sp.nq) continue;
-          const float v = dq[qb][db][e] * sc;
-          if (a.dq_splits > 1) {  // this key range's share, summed by dq_reduce_kernel
-            a.dq_part[((((int64_t)split * a.B + b) * a.H + h) * a.Nq + qr) * D + dcol] = v;
-          } else if (accumulate) {
-            float* p = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
-                       (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
-            *p += v;
-          } else {
-            bf16* p = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh +
-                      (int64_t)(sp.q_row0 + qr) * a.dqs.sn + dcol;
-            *p = (bf16)v;
+          for (int e = 0; e < 16; ++e) {
+            const int qr = q0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (qr < sp.nq) f(qb, db, e, qr, dcol);
           }
         }
-      }
+    };
+    if (a.dq_splits > 1) {  // this key range's share, summed by dq_reduce_kernel
+      each([&](int qb, int db, int e, int qr, int dcol) {
+        a.dq_part[((((int64_t)split * a.B + b) * a.H + h) * a.Nq + qr) * D + dcol] =
+            dq[qb][db][e] * sc;
+      });
+    } else if (accumulate) {
+      float* const base = (float*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)sp.q_row0 * a.dqs.sn;
+      float old[NQB][NDB][16];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) old[qb][db][e] = 0.f;
+      each([&](int qb, int db, int e, int qr, int dcol) {
+        old[qb][db][e] = base[(int64_t)qr * a.dqs.sn + dcol];
+      });
+      // every sum before the first store (a wait for a read issued before a
+      // pending store would wait for that store too); the empty asm keeps
+      // the compiler from sinking the sums next to their stores
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            old[qb][db][e] += dq[qb][db][e] * sc;
+            asm volatile("" : "+v"(old[qb][db][e]));
+          }
+      each([&](int qb, int db, int e, int qr, int dcol) {
+        base[(int64_t)qr * a.dqs.sn + dcol] = old[qb][db][e];
+      });
+    } else {
+      bf16* const base = (bf16*)a.dq + b * a.dqs.sb + h * a.dqs.sh + (int64_t)sp.q_row0 * a.dqs.sn;
+      each([&](int qb, int db, int e, int qr, int dcol) {
+        base[(int64_t)qr * a.dqs.sn + dcol] = (bf16)(dq[qb][db][e] * sc);
+      });
+    }
     return;
   }
   // lane owns query row q0 + 32qb + ln and, per 32-column block db, the runs
