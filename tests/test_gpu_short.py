@@ -110,6 +110,10 @@ def test_short_flags_and_outputs(d):
     assert o32.dtype == torch.float32
     assert max_abs(to_host(o32), o_ref) < 4e-3
     assert max_abs(to_host(lse32), lse_ref) < 1e-3
+    # the backward from that fp32 O (D from the preprocess kernel)
+    g32 = ebw.bwd(q, k, v, o32, do, lse32, scale=scale)
+    torch.cuda.synchronize()
+    check_grads([to_host(t) for t in g32], ref, "bf16", "from fp32 O")
 
 
 def test_short_strided_views():

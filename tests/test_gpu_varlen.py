@@ -178,6 +178,12 @@ def test_packed_flags(lq, lk, d):
     assert torch.equal(full[1], dk2) and torch.equal(full[2], dv2)
     ref = oracle_packed(x, lq, lk, H, d, scale)
     check_grads([to_host(acc) - to_host(base), ref[3], ref[4]], ref[2:], "bf16", "accumulated")
+    # an fp32 O (the packed forward's fp32 output): D from the preprocess kernel
+    o32, lse32 = ebw.fwd_varlen(q, k, v, cq, ck, mq, mk, scale=scale, out_dtype=torch.float32)
+    g32 = ebw.bwd_varlen(q, k, v, o32, do, lse32, cq, ck, mq, mk, scale=scale)
+    torch.cuda.synchronize()
+    assert o32.dtype == torch.float32
+    check_grads([to_host(t) for t in g32], ref[2:], "bf16", "from fp32 O")
 
 
 def test_packed_workload():
