@@ -611,6 +611,21 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   const int q0 = qblk * BM + w * QW;
   const bool wave_active = q0 < sp.nq;
 
+  const int n_kv = min(sp.nkv - kv_lo, a.dq_split_len);
+  const int ntiles = (n_kv + BN - 1) / BN;
+  // direct-to-LDS staging of the key/value tiles (see LdsTileDma); rows
+  // past the end of the key range read as zeros
+  LdsTileDma<D, KS, BN> tk, tv;
+  tk.init(w, lane, a.ks.sn);
+  tv.init(w, lane, a.vs.sn);
+  auto load_tile = [&](int j0, int buf) {
+    const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
+    const uint32_t kbase = lds_address(lds + buf * 2 * L::tile);
+    tk.issue(rk, kbase, w);
+    tv.issue(rv, kbase + 2 * L::tile, w);
+  };
+
   // this wave's Q and dO rows as B operands, with their LSE (log2 units) and
   // D; rows past Nq read as zeros with LSE = +inf
   bf16x8 qreg[NQB][KC], doreg[NQB][KC];
@@ -641,9 +656,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     };
     // the Q rows and LSE go out with the dO rows (one round trip for all);
     // at d = 128 only after D, where holding them early costs more than the
-    // round trip (measured)
+    // round trip (measured, like the early first tile below)
     constexpr bool kQFirst = D != 128;
     if constexpr (kQFirst) load_q();
+    // the first key/value tile goes out with the rows (one round trip;
+    // not at d = 128, as above)
+    if (kQFirst && n_kv > 0) load_tile(0, 0);
     if (a.dq_computes_d) {
       // D_i = dO_i . O_i from the stored bf16 O (the backward preprocess,
       // done here on the rows this wave holds);
@@ -692,8 +710,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   }
   negate_rows(doreg);
 
-  const int n_kv = min(sp.nkv - kv_lo, a.dq_split_len);
-  const int ntiles = (n_kv + BN - 1) / BN;
   f32x16 dq[NQB][NDB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb)
@@ -701,18 +717,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
     for (int db = 0; db < NDB; ++db) dq[qb][db] = f32x16{};
   const float sl2 = a.scale * kLog2e;
 
-  // direct-to-LDS staging of the key/value tiles (see LdsTileDma); rows
-  // past the end of the key range read as zeros
-  LdsTileDma<D, KS, BN> tk, tv;
-  tk.init(w, lane, a.ks.sn);
-  tv.init(w, lane, a.vs.sn);
-  auto load_tile = [&](int j0, int buf) {
-    const auto rk = rows_rsrc(kp + (int64_t)j0 * a.ks.sn, n_kv - j0, 2 * a.ks.sn, 2 * D);
-    const auto rv = rows_rsrc(vp + (int64_t)j0 * a.vs.sn, n_kv - j0, 2 * a.vs.sn, 2 * D);
-    const uint32_t kbase = lds_address(lds + buf * 2 * L::tile);
-    tk.issue(rk, kbase, w);
-    tv.issue(rv, kbase + 2 * L::tile, w);
-  };
 
   // One key/value tile; NEXT: tile it + 1 exists and is staged into the
   // other buffer while this one is computed (waited for before the barrier).
@@ -790,8 +794,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int accumulate) {
   };
   // (a packed sequence without keys: dQ = 0)
   if (n_kv > 0) {
-    load_tile(0, 0);
-    wait_vmem();
+    if (D == 128) load_tile(0, 0);
+    wait_vmem();  // the first tile (at d != 128 requested with the rows)
     __syncthreads();
     using Full = std::integral_constant<int, 2>;
     using Half = std::integral_constant<int, 1>;
