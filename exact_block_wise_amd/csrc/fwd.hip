@@ -12,9 +12,12 @@
 
 #include <type_traits>
 
-// occupancy request (waves per SIMD) of the bf16 forward for d = 64 (its
-// registers then still fit three);
-// d = 80 and 128 ask for two (three would spill)
+// occupancy request (waves per SIMD) of the bf16 forward for d = 64; d = 80
+// and 128 ask for two (three would spill).  At d = 64 the allocation stays
+// at 113 registers, which allows four waves per SIMD, and the 36.9 KB of
+// double-buffered K/V tiles per workgroup also allow four workgroups per
+// compute unit: asking for five cannot be met (the compiler then falls back
+// to its default register budget).
 #ifndef EXATTN_FWD_WAVES
 #define EXATTN_FWD_WAVES 2
 #endif
