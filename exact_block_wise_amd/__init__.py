@@ -141,8 +141,52 @@ def _check_f32_contig(t, shape, name):
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
 
 
+# The C ABI receives pointers and strides, not extents: a tensor smaller than
+# the problem it is passed for would be read or written past its end.  So
+# every tensor is checked against the others here, before any library call.
+
+def _same_device(**named):
+    devs = {n: t.device for n, t in named.items() if t is not None}
+    if len(set(devs.values())) > 1:
+        raise ValueError("all tensors must be on one device, got " +
+                         ", ".join(f"{n}: {d}" for n, d in devs.items()))
+
+
+def _check_ndim(ndim, **named):
+    for n, t in named.items():
+        if t is not None and t.dim() != ndim:
+            raise ValueError(f"{n} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+
+
+def _check_like(ref_name, ref, **named):
+    for n, t in named.items():
+        if t is not None and tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)} "
+                             f"(the shape of {ref_name})")
+
+
+def _check_qkv(q, k, v, kv_axis):
+    """q [..., Nq, ..., d] against k, v: k and v share one shape, and agree
+    with q on every axis but the token axis kv_axis."""
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must have the same shape")
+    for ax in range(q.dim()):
+        if ax != kv_axis and q.shape[ax] != k.shape[ax]:
+            raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ on axis {ax}; "
+                             "only the token axis may differ")
+
+
+def _check_dense(q, k, v, o=None, dout=None, dq=None, dk=None, dv=None, **extra):
+    _check_ndim(4, q=q, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
+    _check_qkv(q, k, v, kv_axis=2)
+    _check_like("q", q, o=o, dout=dout, dq=dq)
+    _check_like("k", k, dk=dk, dv=dv)
+    _same_device(q=q, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv, **extra)
+
+
 def fwd(q, k, v, scale=None, out=None, lse=None, out_dtype=None):
     """Forward pass.  Returns (o [B,H,Nq,d], lse [B,H,Nq] float32)."""
+    _check_dense(q, k, v, o=out, lse=lse)
     lib = load()
     B, H, Nq, d = q.shape
     if out is None:
@@ -161,6 +205,9 @@ def fwd_chunked(q, k, v, n_chunks, scale=None, o_parts=None, lse_parts=None):
 
     Returns (o_parts [n,B,H,Nq,d] float32, lse_parts [n,B,H,Nq] float32).
     """
+    _check_dense(q, k, v, o_parts=o_parts, lse_parts=lse_parts)
+    if n_chunks < 1:
+        raise ValueError("n_chunks must be >= 1")
     lib = load()
     B, H, Nq, d = q.shape
     if o_parts is None:
@@ -178,10 +225,14 @@ def fwd_chunked(q, k, v, n_chunks, scale=None, o_parts=None, lse_parts=None):
 
 def lse_merge(o_parts, lse_parts, out=None, lse=None, out_dtype=torch.bfloat16):
     """Exact merge of partials.  Returns (o [B,H,Nq,d], lse [B,H,Nq])."""
-    lib = load()
+    _check_ndim(5, o_parts=o_parts)
     n, B, H, Nq, d = o_parts.shape
     _check_f32_contig(o_parts, (n, B, H, Nq, d), "o_parts")
     _check_f32_contig(lse_parts, (n, B, H, Nq), "lse_parts")
+    if out is not None and tuple(out.shape) != (B, H, Nq, d):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, Nq, d)}")
+    _same_device(o_parts=o_parts, lse_parts=lse_parts, out=out, lse=lse)
+    lib = load()
     if out is None:
         out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=o_parts.device)
     if lse is None:
@@ -201,6 +252,9 @@ def bwd_workspace_bytes(q, k, accumulate_dq=False) -> int:
 
 def bwd_preprocess(o, dout, dsum=None):
     """D = rowsum(dO * O) in fp32, [B,H,Nq] (the attn_bwd workspace layout)."""
+    _check_ndim(4, o=o, dout=dout)
+    _check_like("o", o, dout=dout)
+    _same_device(o=o, dout=dout, dsum=dsum)
     lib = load()
     B, H, Nq, d = o.shape
     if dsum is None:
@@ -228,6 +282,7 @@ def bwd(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
       bwd_preprocess); o may then be None.
     need_dq / need_dkdv: compute only one half (the other outputs are None).
     """
+    _check_dense(q, k, v, o=o, dout=dout, dq=dq, dk=dk, dv=dv, lse=lse, workspace=workspace)
     lib = load()
     if need_dq and dq is None:
         dq = (torch.zeros_like(q, dtype=torch.float32) if accumulate_dq else torch.empty_like(q))
@@ -278,6 +333,14 @@ def _packed_desc_or_null(t):
     return _packed_desc(t) if t is not None else _Tensor(None, _BF16, 0, 0, 0)
 
 
+def _check_packed(q, k, v, o=None, dout=None, dq=None, dk=None, dv=None, **extra):
+    _check_ndim(3, q=q, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
+    _check_qkv(q, k, v, kv_axis=0)
+    _check_like("q", q, o=o, dout=dout, dq=dq)
+    _check_like("k", k, dk=dk, dv=dv)
+    _same_device(q=q, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv, **extra)
+
+
 def _varlen(q, k, cu_q, cu_kv, max_q, max_kv, scale) -> _Varlen:
     for name, c in (("cu_q", cu_q), ("cu_kv", cu_kv)):
         if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous() or c.dim() != 1:
@@ -294,6 +357,7 @@ def _varlen(q, k, cu_q, cu_kv, max_q, max_kv, scale) -> _Varlen:
 def fwd_varlen(q, k, v, cu_q, cu_kv, max_q, max_kv, scale=None, out=None, lse=None,
                out_dtype=None):
     """Forward over packed sequences.  Returns (o [Tq,H,d], lse [H,Tq] float32)."""
+    _check_packed(q, k, v, o=out, lse=lse, cu_q=cu_q, cu_kv=cu_kv)
     lib = load()
     Tq, H, d = q.shape
     if out is None:
@@ -318,6 +382,8 @@ def bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_kv, max_q, max_kv, scale=None, dq
                dk=None, dv=None, accumulate_dq=False, workspace=None, d_precomputed=False,
                need_dq=True, need_dkdv=True):
     """Backward over packed sequences; arguments as bwd.  Returns (dq, dk, dv)."""
+    _check_packed(q, k, v, o=o, dout=dout, dq=dq, dk=dk, dv=dv, lse=lse, cu_q=cu_q, cu_kv=cu_kv,
+                  workspace=workspace)
     lib = load()
     if need_dq and dq is None:
         dq = (torch.zeros_like(q, dtype=torch.float32) if accumulate_dq else torch.empty_like(q))

@@ -46,13 +46,37 @@ def _run(cmd):
     return out
 
 
+# Host-side sanitizers for the C-ABI layer (argument validation, dispatch):
+# each flag applies to the host pass only, the GPU code is built as usual.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The address-sanitizer runtime of hipcc's clang, which a process that
+    loads a sanitized library must preload (Python itself is not built with
+    it)."""
+    out = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm",
+                                       "bin", "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = out.stdout.strip()
+    if out.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("address-sanitizer runtime not found")
+    return path
+
+
 def build(verbose: bool = False, out_dir: str | None = None,
-          extra_flags: list[str] | None = None) -> str:
+          extra_flags: list[str] | None = None, sanitize: bool = False) -> str:
     """Compile every source and link the shared library; returns its path.
 
     extra_flags are appended to every compile (e.g. -D tile choices).
+    sanitize: build the host code with the address and undefined-behaviour
+    sanitizers (load it with asan_runtime() preloaded).
     """
     cc = hipcc()
+    if sanitize:
+        extra_flags = [*SANITIZE_FLAGS, *(extra_flags or [])]
     obj_dir = os.path.join(out_dir or HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     jobs = []
@@ -67,8 +91,10 @@ def build(verbose: bool = False, out_dir: str | None = None,
     lib = os.path.join(out_dir, "libexattn.so") if out_dir else LIB
     tmp = lib + ".tmp"
     # every symbol resolved at link time: a missing definition fails the build
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined",
-          *[o for o, _ in jobs], "-o", tmp])
+    link_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-shared-libsan"] if sanitize else []
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *link_san,
+          *([] if sanitize else ["-Wl,--no-undefined"]), *[o for o, _ in jobs], "-o", tmp])
     os.replace(tmp, lib)
     if verbose:
         print(f"built {lib}")

@@ -4,6 +4,7 @@
 #include "exattn.h"
 
 #include <math.h>
+#include <string.h>
 
 #include "kernels.hpp"
 
@@ -26,6 +27,9 @@ attn_status check_problem(const attn_problem* p) {
   if (!p) return ATTN_E_INVALID;
   if (p->B < 1 || p->H < 1 || p->Nq < 1 || p->Nkv < 1 || p->d < 1) return ATTN_E_INVALID;
   if (!isfinite(p->scale)) return ATTN_E_INVALID;
+  // the bf16 kernels take the running maximum over raw scores and mask keys
+  // with -inf before scaling, which holds for a positive scale only
+  if (!(p->scale > 0.f)) return ATTN_E_UNSUPPORTED;
   if (!supported_d(p->d)) return ATTN_E_UNSUPPORTED;
   // kernels index (batch, head) pairs with 32-bit integers
   if ((int64_t)p->B * p->H > INT32_MAX) return ATTN_E_UNSUPPORTED;
@@ -78,6 +82,7 @@ attn_status check_varlen(const attn_varlen* p) {
   if (p->n_seq < 1 || p->H < 1 || p->d < 1 || p->max_q < 1 || p->max_kv < 1) return ATTN_E_INVALID;
   if (p->total_q < 0 || p->total_kv < 0 || !p->cu_q || !p->cu_kv) return ATTN_E_INVALID;
   if (!isfinite(p->scale)) return ATTN_E_INVALID;
+  if (!(p->scale > 0.f)) return ATTN_E_UNSUPPORTED;  // as for attn_problem
   if (!supported_d(p->d)) return ATTN_E_UNSUPPORTED;
   if ((int64_t)p->n_seq * p->H > INT32_MAX) return ATTN_E_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(p->cu_q) % 4 || reinterpret_cast<uintptr_t>(p->cu_kv) % 4)
@@ -101,7 +106,11 @@ extern "C" {
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
 
 const char* attn_status_string(attn_status st) {
-  switch (st) {
+  // a C caller may pass any int; reading it as the enum type would be
+  // undefined in C++ for values outside the enumerators' range
+  int v;
+  memcpy(&v, &st, sizeof v);
+  switch (v) {
     case ATTN_OK: return "ATTN_OK";
     case ATTN_E_INVALID: return "ATTN_E_INVALID: invalid argument";
     case ATTN_E_UNSUPPORTED: return "ATTN_E_UNSUPPORTED: head dim, stride or alignment not served";
@@ -274,7 +283,7 @@ attn_status attn_fwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, 
   a.n_chunks = 1; a.chunk_len = p->max_kv;
   a.scale = p->scale;
   a.out_f32 = o.dtype == ATTN_F32;
-  a.cu_q = p->cu_q; a.cu_kv = p->cu_kv; a.total_q = p->total_q;
+  a.cu_q = p->cu_q; a.cu_kv = p->cu_kv; a.total_q = p->total_q; a.total_kv = p->total_kv;
   return from_hip(launch_fwd_bf16(a, p->d, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -326,7 +335,7 @@ attn_status attn_bwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, 
   a.B = p->n_seq; a.H = p->H; a.Nq = p->max_q; a.Nkv = p->max_kv;
   a.scale = p->scale;
   a.o_f32 = o.dtype == ATTN_F32;
-  a.cu_q = p->cu_q; a.cu_kv = p->cu_kv; a.total_q = p->total_q;
+  a.cu_q = p->cu_q; a.cu_kv = p->cu_kv; a.total_q = p->total_q; a.total_kv = p->total_kv;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!pre_done) {
     if (do_dq && !a.o_f32) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "span.hpp"
+
 namespace exattn {
 
 struct Strides {
@@ -31,7 +33,7 @@ struct FwdArgs {
   // 0 (tokens are rows of stride sn) and LSE is [H, total_q].
   const int* cu_q;
   const int* cu_kv;
-  int64_t total_q;
+  int64_t total_q, total_kv;
 };
 
 struct BwdArgs {
@@ -56,24 +58,17 @@ struct BwdArgs {
   // packed variable-length sequences, as in FwdArgs (LSE and D [H, total_q])
   const int* cu_q;
   const int* cu_kv;
-  int64_t total_q;
+  int64_t total_q, total_kv;
 };
 
-// The rows of one (sequence, head) problem: dense [B,H,N,d] tensors, or
-// packed variable-length sequences.
-struct SeqSpan {
-  int q_row0, kv_row0;  // first query / key token of the sequence (0: dense)
-  int nq, nkv;          // its query and key/value lengths
-  int64_t stat0;        // index of its first query row in LSE and D
-};
+// The rows of problem (b, h).  Packed prefix sums are clamped (packed_side)
+// so that no value of cu_q / cu_kv can address rows outside the tensors.
 template <typename Args>
 __device__ __forceinline__ SeqSpan seq_span(const Args& a, int b, int h) {
   SeqSpan s;
   if (a.cu_q) {
-    s.q_row0 = a.cu_q[b];
-    s.nq = a.cu_q[b + 1] - s.q_row0;
-    s.kv_row0 = a.cu_kv[b];
-    s.nkv = a.cu_kv[b + 1] - s.kv_row0;
+    packed_side(a.cu_q[b], a.cu_q[b + 1], a.Nq, a.total_q, s.q_row0, s.nq);
+    packed_side(a.cu_kv[b], a.cu_kv[b + 1], a.Nkv, a.total_kv, s.kv_row0, s.nkv);
     s.stat0 = (int64_t)h * a.total_q + s.q_row0;
   } else {
     s.q_row0 = 0;

@@ -72,7 +72,10 @@ typedef struct {
 } attn_tensor;
 
 /* Problem shape.  scale multiplies Q K^T inside the softmax (1/sqrt(d) for
- * the usual attention). */
+ * the usual attention).  It must be finite (else ATTN_E_INVALID) and
+ * positive (scale <= 0 is ATTN_E_UNSUPPORTED: the bf16 kernels take the
+ * running row maximum over unscaled scores).  Inputs are expected to keep
+ * scale * q.k within the fp32 range; scores are accumulated in fp32. */
 typedef struct {
   int32_t B, H, Nq, Nkv, d;
   float scale;
@@ -230,10 +233,14 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k,
  *      total_kv.  A sequence may be empty on either side (no keys: O = 0,
  *      LSE = -inf, dQ = 0; no queries: dK = dV = 0).
  *   max_q, max_kv: host bounds (>= 1) on every sequence's query and key
- *      lengths; they size the launch.  The arrays are not read on the host:
- *      arrays that break these rules (a length above its bound, sums out of
- *      order or past the tensors) make the kernels address rows outside the
- *      tensors, so the caller must guarantee them.
+ *      lengths; they size the launch.  The arrays are read on the device
+ *      only, and each span is clamped there: rows outside [0, total_q) or
+ *      [0, total_kv) are dropped, a length above its bound is cut to the
+ *      bound, and a pair cu[s] > cu[s+1] is an empty sequence.  So arrays
+ *      that break the rules above give wrong results but never address
+ *      rows outside the tensors.  The arrays themselves must hold n_seq + 1
+ *      readable entries each.
+ * scale as in attn_problem (finite, > 0).
  * BF16 only (F32 is ATTN_E_UNSUPPORTED); d in {64, 80, 128}.  Sequences with
  * both lengths <= 32 take the packed-tile kernels, longer ones the general
  * kernels (the resident-query dK/dV and split-key dQ variants are not used).

@@ -76,6 +76,13 @@ def test_fwd_validation(lib):
     assert fwd(lib, p=P(B=0)) == INVALID
     assert fwd(lib, p=P(Nkv=0)) == INVALID
     assert fwd(lib, p=P(scale=float("nan"))) == INVALID
+    # the bf16 kernels need a positive scale (running maximum over unscaled
+    # scores, keys masked with -inf before scaling)
+    for bad in (0.0, -0.0, -0.125, -1e-30, float("-inf")):
+        assert fwd(lib, p=P(scale=bad)) in (UNSUPPORTED, INVALID)
+        assert fwd(lib, p=P(scale=bad, d=96)) in (UNSUPPORTED, INVALID)
+    assert fwd(lib, p=P(scale=0.0)) == UNSUPPORTED
+    assert fwd(lib, p=P(scale=-0.125)) == UNSUPPORTED
     assert fwd(lib, p=P(d=96)) == UNSUPPORTED
     assert fwd(lib, p=P(d=32)) == UNSUPPORTED
     assert fwd(lib, q=T(ptr=0)) == INVALID
@@ -144,6 +151,8 @@ def test_bwd_validation(lib):
     assert bwd(lib, ws_bytes=1024) == WORKSPACE
     assert bwd(lib, ws=FAKE + 128) == WORKSPACE          # not 256-byte aligned
     assert bwd(lib, p=P(d=48)) == UNSUPPORTED
+    assert bwd(lib, p=P(scale=0.0)) == UNSUPPORTED
+    assert bwd(lib, p=P(scale=-1.0)) == UNSUPPORTED
     assert bwd(lib, o=T(dtype=0), dq=T(dtype=0), flags=1, ws_bytes=0) == WORKSPACE
 
 
@@ -189,6 +198,8 @@ def test_varlen_validation(lib):
     assert fwd_v(p=VL(cu_q=FAKE + 2)) == UNSUPPORTED
     assert fwd_v(p=VL(d=96)) == UNSUPPORTED
     assert fwd_v(p=VL(scale=float("inf"))) == INVALID
+    assert fwd_v(p=VL(scale=0.0)) == UNSUPPORTED
+    assert fwd_v(p=VL(scale=-0.125)) == UNSUPPORTED
     assert fwd_v(lse=0) == INVALID
     assert fwd_v(q=PT(dtype=0)) == INVALID                       # mixed dtypes
     assert lib.attn_fwd_varlen(ctypes.byref(VL()), PT(dtype=0), PT(dtype=0), PT(dtype=0),
