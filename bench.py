@@ -41,7 +41,10 @@ def parse():
                     help="one workload only (default: the ViT-B headline line, with every "
                          "other workload summarised under other_workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle work for the headline workload's CPU baseline")
+    ap.add_argument("--other-cpu-seconds", type=float, default=4.0,
+                    help="oracle work for each other workload's CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for the HBM "
                          "counter scale factors)")
@@ -328,43 +331,77 @@ def upload(w, torch):
     return dev
 
 
-def cpu_baseline(w, budget_s):
-    """The fp64 oracle on the host cores, over whole heads of the same
-    workload until about budget_s seconds of work; scaled to TFLOP/s."""
-    import oracle
+def _oracle_head_inputs(w, b, h):
     from exact_block_wise_amd import synth
+    if is_packed(w):
+        n = w.lens[b]
+        return {t: synth.head_tensor(w.cid, t, b, h, w.H, n, w.d, w.dtype)
+                for t in ("q", "k", "v", "do")}
+    return synth.workload_head(w, b, h)
+
+
+def _gpu_head(w, outs, b, h):
+    """One head's outputs from the GPU results, as float64 host arrays."""
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    if is_packed(w):
+        r0, r1 = int(w.cu[b]), int(w.cu[b + 1])
+        return {"o": f(outs["o"][r0:r1, h]), "lse": f(outs["lse"][h, r0:r1]),
+                **{n: f(outs[n][r0:r1, h]) for n in ("dq", "dk", "dv")}}
+    return {n: f(outs[n][b, h]) for n in ("o", "lse", "dq", "dk", "dv")}
+
+
+def cpu_baseline(w, budget_s, outs=None, repeats=1):
+    """The fp64 oracle on the host cores, over whole heads of the same
+    workload until about budget_s seconds of work; scaled to TFLOP/s.
+    With the GPU outputs of the step (outs), the same oracle results also
+    give the GPU's errors on those heads (outside any timed region).  With
+    repeats > 1 the sample is timed that many times and the median taken."""
+    import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i["num_threads"] for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
-    heads, t_work, flops = 0, 0.0, 0.0
     if is_packed(w):
         order = [(s_, h) for s_ in range(len(w.lens)) for h in range(w.H)]
     else:
         order = [(b, h) for b in range(w.B) for h in range(w.H)]
-    while t_work < budget_s and heads < len(order):
+    # spread the sample over the batch: heads taken with a stride
+    stride = max(1, len(order) // 64)
+    order = order[::stride] + [x for i, x in enumerate(order) if i % stride]
+    err = {"max_abs": {}, "max_ref": {}, "sq_diff": {}, "sq_ref": {}}
+    heads, t_work, flops, times = 0, 0.0, 0.0, []
+    while heads < len(order) and (t_work < budget_s or heads == 0):
         b, h = order[heads]
-        if is_packed(w):
-            n = w.lens[b]
-            x = {t: synth.head_tensor(w.cid, t, b, h, w.H, n, w.d, w.dtype)
-                 for t in ("q", "k", "v", "do")}
-            flops += 14.0 * n * n * w.d
-        else:
-            x = synth.workload_head(w, b, h)
-            flops += 14.0 * w.Nq * w.Nkv * w.d
-        t0 = time.perf_counter()
-        if w.chunks > 1:
-            L = w.Nkv // w.chunks
-            o, lse, _, _ = oracle.head_chunked_fwd(x["q"], x["k"], x["v"], w.scale,
-                                                   list(range(0, w.Nkv + 1, L)))
-            oracle.head_chunked_bwd(x["q"], x["k"], x["v"], x["do"], w.scale,
-                                    list(range(0, w.Nkv + 1, L)), o, lse)
-        else:
-            oracle.head_fwd(x["q"], x["k"], x["v"], w.scale)
-            oracle.head_bwd(x["q"], x["k"], x["v"], x["do"], w.scale)
-        t_work += time.perf_counter() - t0
+        x = _oracle_head_inputs(w, b, h)
+        n_q, n_kv = (w.lens[b], w.lens[b]) if is_packed(w) else (w.Nq, w.Nkv)
+        flops += 14.0 * n_q * n_kv * w.d
+        per = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            if w.chunks > 1:
+                L = w.Nkv // w.chunks
+                bounds = list(range(0, w.Nkv + 1, L))
+                o, lse, _, _ = oracle.head_chunked_fwd(x["q"], x["k"], x["v"], w.scale, bounds)
+                g = oracle.head_chunked_bwd(x["q"], x["k"], x["v"], x["do"], w.scale, bounds, o,
+                                            lse)
+            else:
+                o, lse = oracle.head_fwd(x["q"], x["k"], x["v"], w.scale)
+                g = oracle.head_bwd(x["q"], x["k"], x["v"], x["do"], w.scale)
+            per.append(time.perf_counter() - t0)
+        times.append(per)
+        t_work += float(np.median(per))
         heads += 1
+        if outs is not None:
+            got = _gpu_head(w, outs, b, h)
+            for name, ref in zip(("o", "lse", "dq", "dk", "dv"), (o, lse, *g)):
+                dif = got[name] - ref
+                err["max_abs"][name] = max(err["max_abs"].get(name, 0.0), float(np.abs(dif).max()))
+                err["max_ref"][name] = max(err["max_ref"].get(name, 0.0), float(np.abs(ref).max()))
+                err["sq_diff"][name] = err["sq_diff"].get(name, 0.0) + float((dif * dif).sum())
+                err["sq_ref"][name] = err["sq_ref"].get(name, 0.0) + float((ref * ref).sum())
+    if repeats > 1:
+        t_work = float(np.median([sum(t[i] for t in times) for i in range(repeats)]))
     cpu_model = "unknown"
     try:
         for ln in open("/proc/cpuinfo"):
@@ -373,13 +410,28 @@ def cpu_baseline(w, budget_s):
                 break
     except OSError:
         pass
-    return {"value": round(flops / t_work / 1e12, 6), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
-            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
-            "numpy": __import__("numpy").__version__,
-            "sample": f"{heads} of {len(order)} heads " +
-                      ("(sequence, head)" if is_packed(w) else "(b, h)") +
-                      f" of {w.name}, fwd+bwd in fp64 NumPy, {t_work:.1f} s"}
+    out = {"value": round(flops / t_work / 1e12, 6), "unit": "TFLOP/s",
+           "cores": threads, "kind": "oracle",
+           "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+           "numpy": __import__("numpy").__version__,
+           "seconds": round(t_work, 3),
+           "sample": f"{heads} of {len(order)} heads " +
+                     ("(sequence, head)" if is_packed(w) else "(b, h)") +
+                     f" of {w.name}, fwd+bwd in fp64 NumPy, {t_work:.2f} s" +
+                     (f" (median of {repeats} timings)" if repeats > 1 else "")}
+    errors = None
+    if outs is not None:
+        sq = err["sq_ref"]
+        if w.dtype == "f32":
+            errors = {f"{n}_rel_inf": err["max_abs"][n] / max(err["max_ref"][n], 1e-300)
+                      for n in ("o", "lse", "dq", "dk", "dv")}
+        else:
+            errors = {"o_max_abs": err["max_abs"]["o"], "lse_max_abs": err["max_abs"]["lse"],
+                      **{f"{n}_rel_fro": (err["sq_diff"][n] / sq[n]) ** 0.5 if sq[n] else 0.0
+                         for n in ("dq", "dk", "dv")}}
+        errors = {k: float(f"{v:.3e}") for k, v in errors.items()}
+        errors["heads"] = heads
+    return out, errors
 
 
 def run_workload(w, steps, warmup):
@@ -546,7 +598,7 @@ def run_workload(w, steps, warmup):
         "kernels": kernels,
         "roofline": roof,
     }
-    return line
+    return line, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
 # every workload of the default run, the headline first
@@ -556,11 +608,23 @@ ALL_WORKLOADS = ["vit_b", "vit_l", "vit_h14", "xattn", "vit_b_temporal", "vit_b_
 
 def summary(line):
     r = line["roofline"]
-    return {"value": line["value"], "unit": line["unit"], "pct_of_peak": line["pct_of_peak"],
-            "ms_per_step": line["ms_per_step"], "step_ms_stats": line["step_ms_stats"],
-            "steps": line["steps"], "warmup": line["warmup"], "dtype": line["dtype"],
-            "config": line["config"],
-            "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac")}}
+    out = {"value": line["value"], "unit": line["unit"], "pct_of_peak": line["pct_of_peak"],
+           "ms_per_step": line["ms_per_step"], "step_ms_stats": line["step_ms_stats"],
+           "steps": line["steps"], "warmup": line["warmup"], "dtype": line["dtype"],
+           "config": line["config"],
+           "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac")}}
+    for k in ("cpu_baseline", "oracle_errors"):
+        if k in line:
+            out[k] = line[k]
+    return out
+
+
+def add_oracle_leg(line, w, outs, budget_s, repeats=1):
+    """The CPU oracle baseline and the GPU's errors against it on the same
+    heads, both computed after the timed region."""
+    import torch
+    torch.cuda.synchronize()
+    line["cpu_baseline"], line["oracle_errors"] = cpu_baseline(w, budget_s, outs, repeats)
 
 
 def main():
@@ -586,18 +650,26 @@ def main():
     ebw.load()  # fails loudly without the built library
 
     w = find_workload(args.workload or ALL_WORKLOADS[0])
-    line = run_workload(w, args.steps, args.warmup)
+    line, outs = run_workload(w, args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        add_oracle_leg(line, w, outs, args.cpu_seconds, 3 if w.name == "tiny_f32" else 1)
+    del outs
     if args.workload is None:
         # the default run also measures every other workload (20 steps each),
-        # each summarised in one entry; a failure there is reported, not fatal
+        # each summarised in one entry with its own oracle baseline and
+        # errors; a failure there is reported, not fatal
         others = {}
         for name in ALL_WORKLOADS[1:]:
             # the latency-bound fp32 case gets more repetitions (50 warm-up, 200 timed)
             steps, warm = (200, 50) if name == "tiny_f32" else (20, 5)
             try:
-                others[name] = summary(run_workload(find_workload(name), steps, warm))
+                wo = find_workload(name)
+                lo, outs = run_workload(wo, steps, warm)
+                if not args.no_cpu_baseline:
+                    add_oracle_leg(lo, wo, outs, args.other_cpu_seconds,
+                                   3 if name == "tiny_f32" else 1)
+                del outs
+                others[name] = summary(lo)
             except Exception as e:  # noqa: BLE001 - reported in the line
                 others[name] = {"error": f"{type(e).__name__}: {e}"[:300]}
             torch.cuda.empty_cache()

@@ -5,8 +5,8 @@ may import this package; the HIP library and its binding never do.
 """
 from .attention import (brute_fwd, head_bwd, head_chunked_bwd,
                         head_chunked_fwd, head_fwd, head_lse, head_scores,
-                        lse_merge, ref_bwd, ref_fwd)
+                        lse_merge, ref_bwd, ref_fwd, stack_bwd, stack_fwd)
 
 __all__ = ["brute_fwd", "head_bwd", "head_chunked_bwd", "head_chunked_fwd",
            "head_fwd", "head_lse", "head_scores", "lse_merge", "ref_bwd",
-           "ref_fwd"]
+           "ref_fwd", "stack_bwd", "stack_fwd"]

@@ -165,6 +165,53 @@ def head_chunked_bwd(q, k, v, do, scale, bounds, o, lse):
 
 
 # --------------------------------------------------------------------------
+# A stack of independent heads: the same definition, one matrix product per
+# head through NumPy's stacked matmul.  Used where a workload has too many
+# small heads for a Python loop over head_fwd / head_bwd (divided space-time
+# attention: tens of thousands of 8-token sequences).
+# --------------------------------------------------------------------------
+
+def _kt(k):
+    """K^T of every head of a stack [n, N, d] -> [n, d, N]."""
+    return np.swapaxes(k, -1, -2)
+
+
+def stack_fwd(q, k, v, scale):
+    """(O [n,Nq,d], LSE [n,Nq]) of n independent heads, q [n,Nq,d],
+    k and v [n,Nkv,d]: per head S = scale Q K^T, LSE_i = ln sum_j exp(S_ij),
+    O = exp(S - LSE) V.  An empty key set gives O = 0, LSE = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, nq, nkv = q.shape[0], q.shape[1], k.shape[1]
+    if nkv == 0:
+        return np.zeros((n, nq, v.shape[2])), np.full((n, nq), -np.inf)
+    s = float(scale) * (q @ _kt(k))
+    m = s.max(axis=2)
+    lse = m + np.log(np.exp(s - m[:, :, None]).sum(axis=2))
+    p = np.exp(s - lse[:, :, None])
+    return p @ v, lse
+
+
+def stack_bwd(q, k, v, do, scale):
+    """(dQ, dK, dV) of n independent heads for L = sum(dO * O); the closed
+    form of head_bwd applied to every head of the stack."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    if k.shape[1] == 0:
+        return np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    s = float(scale) * (q @ _kt(k))
+    m = s.max(axis=2)
+    lse = m + np.log(np.exp(s - m[:, :, None]).sum(axis=2))
+    p = np.exp(s - lse[:, :, None])
+    pt = np.swapaxes(p, -1, -2)
+    dv = pt @ do
+    dp = do @ _kt(v)
+    dsum = (p * dp).sum(axis=2)
+    ds = p * (dp - dsum[:, :, None])
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (np.swapaxes(ds, -1, -2) @ q)
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
 # [B, H, N, d] wrappers: one head at a time
 # --------------------------------------------------------------------------
 

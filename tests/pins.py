@@ -285,3 +285,43 @@ def chunked_bwd_vs_unsplit(head_bwd, head_chunked_fwd, head_chunked_bwd, seeds=r
         for a, b in zip(got, ref):
             worst = max(worst, _maxdiff(a, b))
     return worst
+
+
+# ----------------------------------------------------------------- stacks
+
+@_safe
+def stack_vs_brute(stack_fwd, brute_fwd, n_cases=8):
+    """Stacks of 1-5 tiny random heads: every head against pure-Python loops
+    over its own rows only."""
+    worst = 0.0
+    for seed in range(n_cases):
+        g = _rng(100 + seed)
+        n = int(g.integers(1, 6))
+        nq, nkv, d = int(g.integers(1, 7)), int(g.integers(1, 7)), int(g.integers(1, 5))
+        q, k, v = (g.standard_normal((n, m, d)) for m in (nq, nkv, nkv))
+        scale = float(g.uniform(0.2, 1.5))
+        o, lse = stack_fwd(q, k, v, scale)
+        for i in range(n):
+            ob, lb = brute_fwd(q[i].tolist(), k[i].tolist(), v[i].tolist(), scale)
+            worst = max(worst, _maxdiff(o[i], ob), _maxdiff(lse[i], lb))
+    return worst
+
+
+@_safe
+def stack_bwd_vs_autograd(stack_bwd, seeds=(0, 1, 2)):
+    """Gradients of a stack of heads against torch autograd (fp64, CPU) of
+    the naive definition, summed loss over all heads."""
+    import torch
+    worst = 0.0
+    for seed in seeds:
+        g = _rng(200 + seed)
+        n, nq, nkv, d = 3, int(g.integers(1, 6)), int(g.integers(1, 6)), int(g.integers(1, 5))
+        q, k, v, do = (g.standard_normal((n, m, d)) for m in (nq, nkv, nkv, nq))
+        scale = float(g.uniform(0.3, 1.2))
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        o = torch.softmax(scale * tq @ tk.transpose(1, 2), dim=2) @ tv
+        (o * torch.tensor(do)).sum().backward()
+        got = stack_bwd(q, k, v, do, scale)
+        for x, t in zip(got, (tq, tk, tv)):
+            worst = max(worst, _maxdiff(x, t.grad.numpy()))
+    return worst

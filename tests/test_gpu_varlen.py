@@ -16,6 +16,7 @@ import torch
 
 import oracle
 from exact_block_wise_amd import synth
+import full_compare
 from gpu_util import check_grads, max_abs, to_dev, to_host, TOL_LSE_ABS, TOL_O_ABS
 
 pytestmark = pytest.mark.gpu
@@ -187,11 +188,12 @@ def test_packed_flags(lq, lk, d):
 
 
 def test_packed_workload():
-    """The packed mixed image / video batch the benchmark times: sampled
-    (sequence, head) problems of every length against the oracle."""
+    """The packed mixed image / video batch the benchmark times: every
+    (sequence, head) problem against the oracle."""
     w = synth.PACKED_WORKLOADS["vit_b_packed"]
-    _say(f"packed workload {w.name}: upload")
-    dev = {n: to_dev(synth.packed_tensor(w, n), "bf16") for n in ("q", "k", "v", "do")}
+    _say(f"packed workload {w.name}: generate and upload")
+    host = {n: synth.packed_tensor(w, n) for n in ("q", "k", "v", "do")}
+    dev = {n: to_dev(host[n], "bf16") for n in ("q", "k", "v", "do")}
     cq = torch.from_numpy(w.cu).cuda()
     mx = max(w.lens)
     o, lse = ebw.fwd_varlen(dev["q"], dev["k"], dev["v"], cq, cq, mx, mx, scale=w.scale)
@@ -199,20 +201,8 @@ def test_packed_workload():
                                 scale=w.scale)
     torch.cuda.synchronize()
     _say(f"packed workload {w.name}: GPU done")
-    for t in (o, lse, dq, dk, dv):
-        assert bool(torch.isfinite(t.float()).all())
-    g = np.random.Generator(np.random.PCG64(w.cid))
-    errs = []
-    for s in (0, 1, 2, 3, 29, 30, 31):            # every length: 1568, 784, 392, 196
-        h = int(g.integers(w.H))
-        n, r0 = w.lens[s], int(w.cu[s])
-        x = {t: synth.head_tensor(w.cid, t, s, h, w.H, n, w.d, w.dtype)
-             for t in ("q", "k", "v", "do")}
-        o_ref, lse_ref = oracle.head_fwd(x["q"], x["k"], x["v"], w.scale)
-        rows = slice(r0, r0 + n)
-        assert max_abs(to_host(o[rows, h]), o_ref) <= TOL_O_ABS
-        assert max_abs(to_host(lse[h, rows]), lse_ref) <= TOL_LSE_ABS
-        ref = oracle.head_bwd(x["q"], x["k"], x["v"], x["do"], w.scale)
-        errs += check_grads([to_host(t[rows, h]) for t in (dq, dk, dv)], ref, "bf16",
-                            f"{w.name}[{s},{h}]")
-    _say(f"  sampled grad errors max {max(errs):.2e}")
+    errs = full_compare.compare_packed(w, host, {"o": o, "lse": lse, "dq": dq, "dk": dk,
+                                                 "dv": dv}, say=_say)
+    assert errs.heads == len(w.lens) * w.H
+    full_compare.log_errors(_say, f"{w.name}, all {errs.heads} problems", errs, "bf16")
+    errs.check("bf16", w.name)

@@ -74,6 +74,58 @@ def test_batched_wrappers_match_heads():
                 assert np.array_equal(x, y[b, h])
 
 
+# --------------------------------------------------------------------------
+# The stacked functions (many independent heads in one call) carry every pin
+# of the per-head ones, through one-head stacks, plus a check that heads of
+# a stack never mix.
+# --------------------------------------------------------------------------
+
+def _one_head_fwd(q, k, v, scale):
+    o, lse = A.stack_fwd(np.asarray(q)[None], np.asarray(k)[None], np.asarray(v)[None], scale)
+    return o[0], lse[0]
+
+
+def _one_head_bwd(q, k, v, do, scale):
+    g = A.stack_bwd(*(np.asarray(x)[None] for x in (q, k, v, do)), scale)
+    return tuple(x[0] for x in g)
+
+
+def test_stack_pins():
+    assert pins.fwd_vs_brute(_one_head_fwd, A.brute_fwd) < 1e-13
+    assert pins.fwd_golden(_one_head_fwd) < TOL
+    assert pins.fwd_closed_forms(_one_head_fwd) < TOL
+    assert pins.fwd_invariants(_one_head_fwd) < 1e-11
+    assert pins.bwd_finite_differences(_one_head_fwd, _one_head_bwd) < 1e-7
+    assert pins.bwd_vs_autograd(_one_head_bwd) < TOL
+    assert pins.bwd_golden(_one_head_bwd) < TOL
+    assert pins.bwd_invariants(_one_head_bwd) < 1e-12
+
+
+def test_stack_heads_stay_separate():
+    assert pins.stack_vs_brute(A.stack_fwd, A.brute_fwd) < 1e-13
+    assert pins.stack_bwd_vs_autograd(A.stack_bwd) < TOL
+    o, lse = A.stack_fwd(np.ones((2, 3, 2)), np.zeros((2, 0, 2)), np.zeros((2, 0, 2)), 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def _stack_fwd_heads_mixed(q, k, v, scale):
+    # K^T taken over the wrong axes: head n meets the keys of other heads
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    s = float(scale) * np.einsum("nid,mjd->nij", q, k[::-1])
+    lse = np.log(np.exp(s).sum(axis=2))
+    return np.exp(s - lse[:, :, None]) @ v, lse
+
+
+def _stack_bwd_sum_over_heads(q, k, v, do, scale):
+    dq, dk, dv = A.stack_bwd(q, k, v, do, scale)
+    return dq, dk, dv + dv.sum(axis=0, keepdims=True) - dv  # every head gets the total
+
+
+def test_stack_pins_catch_mixed_heads():
+    assert pins.stack_vs_brute(_stack_fwd_heads_mixed, A.brute_fwd) > 1e-6
+    assert pins.stack_bwd_vs_autograd(_stack_bwd_sum_over_heads) > 1e-6
+
+
 def test_empty_key_set():
     o, lse = A.head_fwd(np.ones((3, 2)), np.zeros((0, 2)), np.zeros((0, 2)), 1.0)
     assert np.all(o == 0) and np.all(np.isneginf(lse))
