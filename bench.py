@@ -627,6 +627,11 @@ def add_oracle_leg(line, w, outs, budget_s, repeats=1):
     line["cpu_baseline"], line["oracle_errors"] = cpu_baseline(w, budget_s, outs, repeats)
 
 
+def progress(msg):
+    """A progress line on stderr (the JSON result alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.make_mfma_profile:
@@ -651,8 +656,10 @@ def main():
 
     w = find_workload(args.workload or ALL_WORKLOADS[0])
     line, outs = run_workload(w, args.steps, args.warmup)
+    progress(f"{w.name}: {line['ms_per_step']:.4f} ms per step, {line['value']:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
         add_oracle_leg(line, w, outs, args.cpu_seconds, 3 if w.name == "tiny_f32" else 1)
+        progress(f"{w.name}: oracle leg {line['oracle_errors']}")
     del outs
     if args.workload is None:
         # the default run also measures every other workload (20 steps each),
@@ -665,9 +672,11 @@ def main():
             try:
                 wo = find_workload(name)
                 lo, outs = run_workload(wo, steps, warm)
+                progress(f"{name}: {lo['ms_per_step']:.4f} ms per step, {lo['value']:.2f} TFLOP/s")
                 if not args.no_cpu_baseline:
                     add_oracle_leg(lo, wo, outs, args.other_cpu_seconds,
                                    3 if name == "tiny_f32" else 1)
+                    progress(f"{name}: oracle leg {lo['oracle_errors']}")
                 del outs
                 others[name] = summary(lo)
             except Exception as e:  # noqa: BLE001 - reported in the line
