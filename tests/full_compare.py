@@ -212,6 +212,13 @@ def compare_packed(w, inputs, outputs, say=print, threads=None):
     return total
 
 
+# one line per compared workload, printed again in pytest's terminal summary
+# (tests/conftest.py) so that a quiet run's log still records the errors
+REPORT = []
+
+
 def log_errors(say, what, errs, dtype):
     s = errs.summary(dtype)
-    say(f"  {what}: " + ", ".join(f"{k} {v:.3e}" for k, v in s.items()))
+    line = f"{what}: " + ", ".join(f"{k} {v:.3e}" for k, v in s.items())
+    REPORT.append(line)
+    say("  " + line)
