@@ -8,6 +8,7 @@ or fails to load, every call raises.
 
     o, lse = fwd(q, k, v)                        # [B,H,N,d] tensors
     dq, dk, dv = bwd(q, k, v, o, do, lse)
+    dq, dk, dv = bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv)  # no workspace argument
     o_parts, lse_parts = fwd_chunked(q, k, v, n_chunks=8)
     o, lse = lse_merge(o_parts, lse_parts)
     o, lse = fwd_varlen(q, k, v, cu_q, cu_kv, max_q, max_kv)   # packed [T,H,d]
@@ -21,7 +22,7 @@ import os
 
 import torch  # imported first so the library binds to torch's HIP runtime
 
-__all__ = ["fwd", "fwd_chunked", "lse_merge", "bwd", "bwd_preprocess",
+__all__ = ["fwd", "fwd_chunked", "lse_merge", "bwd", "bwd_preprocess", "bwd_noalloc",
            "bwd_workspace_bytes", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
            "ExattnError", "library_path", "load", "ABI_VERSION",
            "BWD_DQ_ACCUMULATE", "BWD_D_PRECOMPUTED", "BWD_NO_DQ", "BWD_NO_DKDV"]
@@ -95,6 +96,8 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_preprocess.argtypes = [P, T, T, fp, vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [P, T, T, T, T, T, fp, T, T, T, vp, sz, u32, vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [P, T, T, T, T, T, fp, T, T, T, u32, vp]
     V = ctypes.POINTER(_Varlen)
     lib.attn_fwd_varlen.restype = ctypes.c_int
     lib.attn_fwd_varlen.argtypes = [V, T, T, T, T, fp, vp]
@@ -309,6 +312,33 @@ def bwd(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
                         _desc_or_null(dk if need_dkdv else None),
                         _desc_or_null(dv if need_dkdv else None),
                         workspace.data_ptr(), ws_bytes, flags, _stream(q.device)))
+    return (dq if need_dq else None, dk if need_dkdv else None, dv if need_dkdv else None)
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale=None, accumulate_dq=False,
+                d_precomputed=False, need_dq=True, need_dkdv=True):
+    """attn_bwd_noalloc: the backward with the library's own per-GPU scratch
+    as workspace (the C call allocates nothing).  The outputs are passed in;
+    d_precomputed: the scratch holds D from the previous such call with the
+    same o and dout.  Arguments otherwise as bwd.  Returns (dq, dk, dv)."""
+    _check_dense(q, k, v, o=o, dout=dout, dq=dq, dk=dk, dv=dv, lse=lse)
+    lib = load()
+    B, H, Nq, d = q.shape
+    _check_f32_contig(lse, (B, H, Nq), "lse")
+    flags = ((BWD_DQ_ACCUMULATE if accumulate_dq else 0) |
+             (BWD_D_PRECOMPUTED if d_precomputed else 0) |
+             (0 if need_dq else BWD_NO_DQ) | (0 if need_dkdv else BWD_NO_DKDV))
+    p = _problem(q, k, scale)
+    _check("attn_bwd_noalloc",
+           lib.attn_bwd_noalloc(ctypes.byref(p), _desc(q), _desc(k), _desc(v), _desc_or_null(o),
+                                _desc(dout), lse.data_ptr(),
+                                _desc_or_null(dq if need_dq else None),
+                                _desc_or_null(dk if need_dkdv else None),
+                                _desc_or_null(dv if need_dkdv else None), flags,
+                                _stream(q.device)))
     return (dq if need_dq else None, dk if need_dkdv else None, dv if need_dkdv else None)
 
 

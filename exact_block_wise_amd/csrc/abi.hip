@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 using namespace exattn;
@@ -97,6 +99,108 @@ Strides packed_strides(const attn_tensor& t) { return Strides{0, t.sh, t.sn}; }
 
 size_t varlen_dsum_bytes(const attn_varlen* p) {
   return round_up((size_t)p->H * p->total_q * sizeof(float), kWsAlign);
+}
+
+// attn_bwd's validation and, when `launch` is set, its launches.  With
+// launch false it returns after the host-side checks (nothing enqueued).
+attn_status bwd_dense(const attn_problem* p, const attn_tensor& q, const attn_tensor& k,
+                      const attn_tensor& v, const attn_tensor& o, const attn_tensor& dout,
+                      const float* lse, const attn_tensor& dq, const attn_tensor& dk,
+                      const attn_tensor& dv, void* workspace, size_t workspace_bytes,
+                      uint32_t flags, void* stream, bool launch) {
+  constexpr uint32_t kAll = ATTN_BWD_DQ_ACCUMULATE | ATTN_BWD_D_PRECOMPUTED | ATTN_BWD_NO_DQ |
+                            ATTN_BWD_NO_DKDV;
+  if (flags & ~kAll) return ATTN_E_INVALID;
+  const bool acc = flags & ATTN_BWD_DQ_ACCUMULATE;
+  const bool pre_done = flags & ATTN_BWD_D_PRECOMPUTED;
+  const bool do_dq = !(flags & ATTN_BWD_NO_DQ);
+  const bool do_dkdv = !(flags & ATTN_BWD_NO_DKDV);
+  if (!do_dq && !do_dkdv) return ATTN_E_INVALID;
+  attn_status st = first_error({check_problem(p), check_tensor(q), check_tensor(k),
+                                check_tensor(v), check_tensor(dout),
+                                pre_done ? ATTN_OK : check_tensor(o),
+                                do_dq ? check_tensor(dq) : ATTN_OK,
+                                do_dkdv ? check_tensor(dk) : ATTN_OK,
+                                do_dkdv ? check_tensor(dv) : ATTN_OK});
+  if (st != ATTN_OK) return st;
+  const int dt = q.dtype;
+  if (k.dtype != dt || v.dtype != dt || dout.dtype != dt) return ATTN_E_INVALID;
+  if (!pre_done && !pre_dtypes_ok(o.dtype, dt)) return ATTN_E_INVALID;
+  if (do_dkdv && (dk.dtype != dt || dv.dtype != dt)) return ATTN_E_INVALID;
+  if (do_dq && (acc ? dq.dtype != ATTN_F32 : dq.dtype != dt)) return ATTN_E_INVALID;
+  if (!lse) return ATTN_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
+  const size_t part_bytes = dq_part_bytes(p, flags);
+  if (!workspace || workspace_bytes < dsum_bytes(p) + part_bytes) return ATTN_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return ATTN_E_WORKSPACE;
+  if (!launch) return ATTN_OK;
+
+  BwdArgs a{};
+  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.o = o.ptr; a.dout = dout.ptr; a.lse = lse;
+  a.dq = dq.ptr; a.dk = dk.ptr; a.dv = dv.ptr;
+  a.qs = strides_of(q); a.ks = strides_of(k); a.vs = strides_of(v); a.os = strides_of(o);
+  a.dos = strides_of(dout); a.dqs = strides_of(dq); a.dks = strides_of(dk);
+  a.dvs = strides_of(dv);
+  a.dsum = static_cast<float*>(workspace);
+  a.dq_part = part_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    dsum_bytes(p))
+                         : nullptr;
+  a.dq_splits = 1;
+  a.dq_split_len = p->Nkv;
+  a.B = p->B; a.H = p->H; a.Nq = p->Nq; a.Nkv = p->Nkv;
+  a.scale = p->scale;
+  a.o_f32 = o.dtype == ATTN_F32;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!pre_done) {
+    if (do_dq && dt == ATTN_BF16 && !a.o_f32) {
+      a.dq_computes_d = 1;  // the bf16 dQ kernel forms D from a bf16 O and runs first
+    } else {
+      const hipError_t e = launch_bwd_pre(a, p->d, dt == ATTN_BF16, s);
+      if (e != hipSuccess) return ATTN_E_HIP;
+    }
+  }
+  if (dt == ATTN_F32) return from_hip(launch_bwd_f32(a, p->d, do_dkdv, do_dq, acc, s));
+  return from_hip(launch_bwd_bf16(a, p->d, do_dkdv, do_dq, acc, s));
+}
+
+// --------------------------------------------------------------------------
+// Scratch of attn_bwd_noalloc: a file-scope device array, one copy per GPU,
+// allocated with the library's code object (so a call allocates nothing).
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and only that address is
+// ever passed to kernels.
+// --------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The scratch address on the device that runs `stream` (the current device
+// for the null stream).
+attn_status scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  const hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return ATTN_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_E_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    hipError_t r = hipGetDevice(&cur);
+    if (r == hipSuccess && cur != dev) r = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (r == hipSuccess) r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (r == hipSuccess) r = back;
+    }
+    g_scratch_err[dev] = r;
+    g_scratch_ptr[dev] = r == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return ATTN_E_HIP;
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -211,58 +315,26 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k, attn_t
                      attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
                      attn_tensor dk, attn_tensor dv, void* workspace, size_t workspace_bytes,
                      uint32_t flags, void* stream) {
-  constexpr uint32_t kAll = ATTN_BWD_DQ_ACCUMULATE | ATTN_BWD_D_PRECOMPUTED | ATTN_BWD_NO_DQ |
-                            ATTN_BWD_NO_DKDV;
-  if (flags & ~kAll) return ATTN_E_INVALID;
-  const bool acc = flags & ATTN_BWD_DQ_ACCUMULATE;
-  const bool pre_done = flags & ATTN_BWD_D_PRECOMPUTED;
-  const bool do_dq = !(flags & ATTN_BWD_NO_DQ);
-  const bool do_dkdv = !(flags & ATTN_BWD_NO_DKDV);
-  if (!do_dq && !do_dkdv) return ATTN_E_INVALID;
-  attn_status st = first_error({check_problem(p), check_tensor(q), check_tensor(k),
-                                check_tensor(v), check_tensor(dout),
-                                pre_done ? ATTN_OK : check_tensor(o),
-                                do_dq ? check_tensor(dq) : ATTN_OK,
-                                do_dkdv ? check_tensor(dk) : ATTN_OK,
-                                do_dkdv ? check_tensor(dv) : ATTN_OK});
-  if (st != ATTN_OK) return st;
-  const int dt = q.dtype;
-  if (k.dtype != dt || v.dtype != dt || dout.dtype != dt) return ATTN_E_INVALID;
-  if (!pre_done && !pre_dtypes_ok(o.dtype, dt)) return ATTN_E_INVALID;
-  if (do_dkdv && (dk.dtype != dt || dv.dtype != dt)) return ATTN_E_INVALID;
-  if (do_dq && (acc ? dq.dtype != ATTN_F32 : dq.dtype != dt)) return ATTN_E_INVALID;
-  if (!lse) return ATTN_E_INVALID;
-  if (reinterpret_cast<uintptr_t>(lse) % 4) return ATTN_E_UNSUPPORTED;
-  const size_t part_bytes = dq_part_bytes(p, flags);
-  if (!workspace || workspace_bytes < dsum_bytes(p) + part_bytes) return ATTN_E_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) return ATTN_E_WORKSPACE;
+  return bwd_dense(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, flags,
+                   stream, true);
+}
 
-  BwdArgs a{};
-  a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.o = o.ptr; a.dout = dout.ptr; a.lse = lse;
-  a.dq = dq.ptr; a.dk = dk.ptr; a.dv = dv.ptr;
-  a.qs = strides_of(q); a.ks = strides_of(k); a.vs = strides_of(v); a.os = strides_of(o);
-  a.dos = strides_of(dout); a.dqs = strides_of(dq); a.dks = strides_of(dk);
-  a.dvs = strides_of(dv);
-  a.dsum = static_cast<float*>(workspace);
-  a.dq_part = part_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                    dsum_bytes(p))
-                         : nullptr;
-  a.dq_splits = 1;
-  a.dq_split_len = p->Nkv;
-  a.B = p->B; a.H = p->H; a.Nq = p->Nq; a.Nkv = p->Nkv;
-  a.scale = p->scale;
-  a.o_f32 = o.dtype == ATTN_F32;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (!pre_done) {
-    if (do_dq && dt == ATTN_BF16 && !a.o_f32) {
-      a.dq_computes_d = 1;  // the bf16 dQ kernel forms D from a bf16 O and runs first
-    } else {
-      const hipError_t e = launch_bwd_pre(a, p->d, dt == ATTN_BF16, s);
-      if (e != hipSuccess) return ATTN_E_HIP;
-    }
-  }
-  if (dt == ATTN_F32) return from_hip(launch_bwd_f32(a, p->d, do_dkdv, do_dq, acc, s));
-  return from_hip(launch_bwd_bf16(a, p->d, do_dkdv, do_dq, acc, s));
+attn_status attn_bwd_noalloc(const attn_problem* p, attn_tensor q, attn_tensor k,
+                             attn_tensor v, attn_tensor o, attn_tensor dout, const float* lse,
+                             attn_tensor dq, attn_tensor dk, attn_tensor dv, uint32_t flags,
+                             void* stream) {
+  // every host-side check first, with a stand-in for the scratch address
+  // (aligned, never dereferenced): a problem whose workspace exceeds the
+  // scratch is ATTN_E_WORKSPACE, and nothing touches the GPU before this
+  const attn_status st = bwd_dense(p, q, k, v, o, dout, lse, dq, dk, dv,
+                                   reinterpret_cast<void*>(kWsAlign), ATTN_NOALLOC_SCRATCH_BYTES,
+                                   flags, stream, false);
+  if (st != ATTN_OK) return st;
+  void* ws = nullptr;
+  const attn_status sst = scratch_for(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (sst != ATTN_OK) return sst;
+  return bwd_dense(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ATTN_NOALLOC_SCRATCH_BYTES, flags,
+                   stream, true);
 }
 
 attn_status attn_fwd_varlen(const attn_varlen* p, attn_tensor q, attn_tensor k, attn_tensor v,

@@ -30,7 +30,8 @@
  *    error other than ATTN_E_HIP has enqueued no work and touched no memory.
  *  - ATTN_E_HIP means a kernel launch was rejected by the HIP runtime; work
  *    enqueued earlier in the same call may have run.
- *  - No call keeps global mutable state, prints, throws or aborts.  Calls on
+ *  - No call prints, throws or aborts, and none keeps global mutable state
+ *    except attn_bwd_noalloc's per-GPU scratch (see there).  Calls on
  *    distinct streams may run concurrently from different host threads.
  *  - Supported: d in {64, 80, 128}; inputs all F32 or all BF16.  bf16 inputs
  *    use bf16 matrix-core products with fp32 accumulation; f32 inputs use
@@ -213,6 +214,35 @@ attn_status attn_bwd(const attn_problem* p, attn_tensor q, attn_tensor k,
                      const float* lse, attn_tensor dq, attn_tensor dk,
                      attn_tensor dv, void* workspace, size_t workspace_bytes,
                      uint32_t flags, void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, flags, results and errors are those of attn_bwd, without the
+ * workspace: the workspace is a device array inside the library, one copy
+ * per GPU, ATTN_NOALLOC_SCRATCH_BYTES (96 MiB) long, held from the library's
+ * first use on that GPU until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on
+ * a GPU looks up that GPU's copy (hipGetSymbolAddress) once.
+ *
+ *   A problem whose attn_bwd_workspace_bytes(p, flags) exceeds the scratch
+ *   returns ATTN_E_WORKSPACE with nothing enqueued (e.g. the 8-way split dQ
+ *   pass of 4 x 32 heads x 128 queries x d = 128 needs 64 MiB + 64 KiB and
+ *   fits; D alone for B*H*Nq rows needs 4 bytes per row).
+ *   ATTN_BWD_D_PRECOMPUTED means: the scratch holds D from the previous
+ *   call on this GPU with the same o and dout (its contents are kept
+ *   between calls; nothing in it needs to start at zero).
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (different streams or host threads) race on it and must
+ *   be ordered by the caller.  ATTN_E_HIP if the scratch cannot be looked up.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+attn_status attn_bwd_noalloc(const attn_problem* p, attn_tensor q, attn_tensor k,
+                             attn_tensor v, attn_tensor o, attn_tensor dout,
+                             const float* lse, attn_tensor dq, attn_tensor dk,
+                             attn_tensor dv, uint32_t flags, void* stream);
 
 /*
  * Packed variable-length sequences ("THD" layout).

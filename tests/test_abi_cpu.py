@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_abi_version", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes",
         "attn_fwd", "attn_fwd_chunked", "attn_lse_merge", "attn_status_string",
-        "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes"])
+        "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
+        "attn_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -219,3 +220,25 @@ def test_varlen_validation(lib):
     assert bwd_v(flags=1) == INVALID                             # accumulate needs fp32 dq
     assert bwd_v(p=VL(max_kv=-3)) == INVALID
     assert fwd_v(p=VL(n_seq=1 << 20, H=1 << 12)) == UNSUPPORTED  # sequences * heads too many
+
+
+def test_bwd_noalloc_validation(lib):
+    """Every host-side check of attn_bwd, then the scratch size; all before
+    the first GPU call (so they run here, without a GPU)."""
+    def call(p=None, flags=0, lse=FAKE, dq=None, dout=None):
+        return lib.attn_bwd_noalloc(ctypes.byref(p or P()), T(), T(), T(), T(), dout or T(), lse,
+                                    dq or T(), T(), T(), flags, None)
+    assert call(flags=16) == INVALID
+    assert call(flags=4 | 8) == INVALID
+    assert call(lse=0) == INVALID
+    assert call(dout=T(dtype=0)) == INVALID
+    assert call(dq=T(dtype=1), flags=1) == INVALID
+    assert call(p=P(d=48)) == UNSUPPORTED
+    assert call(p=P(scale=0.0)) == UNSUPPORTED
+    # the workspace must fit the 96 MiB scratch: D alone for 2^25 rows is 128 MiB
+    big = P(B=1024, H=32, Nq=1024, Nkv=64)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(big), 0) > ebw.NOALLOC_SCRATCH_BYTES
+    assert call(p=big) == WORKSPACE
+    # the cross-attention shape's split dQ partials (64 MiB + D) fit
+    px = P(B=4, H=32, Nq=128, Nkv=32768, d=128)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(px), 0) <= ebw.NOALLOC_SCRATCH_BYTES
