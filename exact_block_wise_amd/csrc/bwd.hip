@@ -230,7 +230,7 @@ __device__ __forceinline__ void negate_rows(bf16x8 (&v)[NCB][KC]) {
 // (0..3) (accumulator entries 4i .. 4i+3); the runs go through this wave's
 // LDS staging rows (`stage`, 32 NCB rows of stride DP + 8) and leave as
 // whole rows (store_staged_rows).
-template <int D, int NCB>
+template <int D, int NCB, bool NT = (EXATTN_NT_OUT != 0)>
 __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, const SeqSpan& sp,
                                            int kw, const f32x16 (&dk)[NCB][(D + 31) / 32],
                                            const f32x16 (&dv)[NCB][(D + 31) / 32], bf16* stage,
@@ -261,7 +261,7 @@ __device__ __forceinline__ void dkdv_store(const BwdArgs& a, int b, int h, const
     const int64_t sn = t == 0 ? a.dks.sn : a.dvs.sn;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-      store_staged_rows<bf16, D, SRS>(stage + 32 * cb * SRS, out + (int64_t)32 * cb * sn, sn,
+      store_staged_rows<bf16, D, SRS, NT>(stage + 32 * cb * SRS, out + (int64_t)32 * cb * sn, sn,
                                       sp.nkv - kw - 32 * cb, lane);
   }
 }

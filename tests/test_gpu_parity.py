@@ -435,3 +435,28 @@ def test_head_offsets_beyond_4gib(Nq, Nkv, d):
                 oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale), "bf16", "far heads")
     del q, do, k, v, o, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_resident_backward_both_halves(d, accumulate):
+    """A short query block against a long key range with both halves in one
+    call (the resident-query dK/dV kernel and the split-key dQ pass with its
+    ordered reduce), against the oracle; with accumulation into an fp32 dQ
+    as well."""
+    B, H, Nq, Nkv = 2, 3, 100, 1000
+    x = synth.random_case(4200 + d, B, H, Nq, Nkv, d, "bf16")
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = ebw.fwd(q, k, v, scale=scale)
+    if accumulate:
+        base = torch.randn(q.shape, dtype=torch.float32, device="cuda")
+        dq = base.clone()
+        _, dk, dv = ebw.bwd(q, k, v, o, do, lse, scale=scale, dq=dq, accumulate_dq=True)
+    else:
+        dq, dk, dv = ebw.bwd(q, k, v, o, do, lse, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.ref_bwd(x["q"], x["k"], x["v"], x["do"], scale)
+    got_dq = to_host(dq) - (to_host(base) if accumulate else 0.0)
+    errs = check_grads([got_dq, to_host(dk), to_host(dv)], ref, "bf16", f"resident d={d}")
+    _say(f"  resident d={d} acc={accumulate}: {['%.2e' % e for e in errs]}")
