@@ -114,7 +114,7 @@ constexpr int NT = 256;
 template <int D>
 struct DkdvLds {
   static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int RS = DP + 8;                          // row stride of Q, dO tiles
+  static constexpr int RS = tile_stride(DP);                  // row stride of Q, dO tiles
   static constexpr int tile = bwdk::BM * RS;
   static constexpr int n_bf16 = 4 * tile;                    // Q, dO x double buffer
   static constexpr int bytes = n_bf16 * 2 + 2 * 2 * bwdk::BM * 4;  // + (LSE, D) x 2
@@ -128,7 +128,7 @@ struct DkdvLds {
 // columns from LDS transpose reads.  Folding D into the accumulator and the
 // sign into V leaves one multiply per score for dS.  Qs / dOs: row-major bf16
 // query rows (row stride rs), lse2s / Ds: their LSE in log2 units and D.
-template <int D, int NCB, bool PIN>
+template <int D, int NCB, bool PIN, bool FIRST = false>
 __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int rs,
                                             const float* lse2s, const float* Ds, int nb,
                                             float sl2, const bf16x8 (&kreg)[NCB][D / 16],
@@ -137,12 +137,6 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
                                             f32x16 (&dv)[NCB][(D + 31) / 32], int lane) {
   constexpr int KC = D / 16, NDB = (D + 31) / 32;
   const int ln = lane & 31, g = lane >> 5;
-  bf16x8 qa[KC], da[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    qa[kc] = load_bf16x8(&Qs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
-    da[kc] = load_bf16x8(&dOs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
-  }
   // D of the accumulator rows: entry 4i + r is query 32nb + 8i + 4g + r
   f32x16 dinit;
 #pragma unroll
@@ -152,16 +146,36 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
     for (int r = 0; r < 4; ++r) dinit[4 * i + r] = d4[r];
   }
   f32x16 s[NCB], e[NCB];
-  prio_mfma();
+  // The Q / dO row operands of all KC d-chunks are read at once, except at
+  // d = 128 with one key block per wave (the one-wave-per-SIMD kernels), where
+  // 16 of them would crowd the vector registers: there they come in two
+  // fenced halves over d.
+  constexpr int PARTS = (NCB == 1 && KC == 8) ? 2 : 1;
+  constexpr int KP = KC / PARTS;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     s[cb] = f32x16{};
     e[cb] = dinit;
+  }
+  prio_mfma();
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      s[cb] = mfma32(qa[kc], kreg[cb][kc], s[cb]);
-      e[cb] = mfma32(da[kc], vneg[cb][kc], e[cb]);
+  for (int part = 0; part < PARTS; ++part) {
+    bf16x8 qa[KP], da[KP];
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int kc = part * KP + j;
+      qa[j] = load_bf16x8(&Qs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
+      da[j] = load_bf16x8(&dOs[(32 * nb + ln) * rs + 16 * kc + 8 * g]);
     }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        const int kc = part * KP + j;
+        s[cb] = mfma32(qa[j], kreg[cb][kc], s[cb]);
+        e[cb] = mfma32(da[j], vneg[cb][kc], e[cb]);
+      }
+    if constexpr (PARTS > 1) __builtin_amdgcn_sched_barrier(0);
   }
   prio_valu();
 #pragma unroll
@@ -198,9 +212,21 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
       const bf16x8 qbv = tr_operand(Qs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        if constexpr (PIN) {
+        // FIRST: the block's first products start the accumulators from zero
+        if constexpr (PIN && FIRST) {
+          if (hh == 0) {
+            mfma32_agpr_zero(dob, pa[cb], dv[cb][db]);
+            mfma32_agpr_zero(qbv, sa[cb], dk[cb][db]);
+          } else {
+            mfma32_agpr(dob, pa[cb], dv[cb][db]);
+            mfma32_agpr(qbv, sa[cb], dk[cb][db]);
+          }
+        } else if constexpr (PIN) {
           mfma32_agpr(dob, pa[cb], dv[cb][db]);
           mfma32_agpr(qbv, sa[cb], dk[cb][db]);
+        } else if constexpr (FIRST) {
+          dv[cb][db] = mfma32(dob, pa[cb], hh == 0 ? f32x16{} : dv[cb][db]);
+          dk[cb][db] = mfma32(qbv, sa[cb], hh == 0 ? f32x16{} : dk[cb][db]);
         } else {
           dv[cb][db] = mfma32(dob, pa[cb], dv[cb][db]);
           dk[cb][db] = mfma32(qbv, sa[cb], dk[cb][db]);
@@ -426,7 +452,7 @@ constexpr int KB = 128;  // keys per workgroup step (4 waves x 32)
 template <int D>
 struct ResLds {
   static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int RS = DP + 8;                           // row stride of Q, dO
+  static constexpr int RS = tile_stride(DP);                  // row stride of Q, dO
   static constexpr int stage = 32 * RS;                       // output rows per wave
   static constexpr int bytes = 2 * resk::QR * RS * 2 + 2 * resk::QR * 4 + 4 * stage * 2;
 };
@@ -511,13 +537,11 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
   f32x16 dk[1][NDB], dv[1][NDB];
   auto block = [&](int kb_) {
     negate_rows(vreg);
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) {
-      dk[0][i] = f32x16{};
-      dv[0][i] = f32x16{};
-    }
+    // the first query block's products start dK and dV from zero (no
+    // clearing of the accumulators per key block)
+    dkdv_qblock<D, 1, kPin, true>(Qs, dOs, RS, lse2s, Ds, 0, sl2, kreg, vreg, dk, dv, lane);
 #pragma unroll 1
-    for (int nb = 0; nb < nqb; ++nb)
+    for (int nb = 1; nb < nqb; ++nb)
       dkdv_qblock<D, 1, kPin>(Qs, dOs, RS, lse2s, Ds, nb, sl2, kreg, vreg, dk, dv, lane);
     if constexpr (kPin) agpr_results_ready();
     // The next block's rows were requested a whole block ago: wait for them
@@ -567,7 +591,7 @@ constexpr int NT = 256;
 template <int D>
 struct DqLds {
   static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int KS = DP + 8;
+  static constexpr int KS = tile_stride(DP);
   static constexpr int tile = dqk::BN * KS;
   static constexpr int bytes = 4 * tile * 2;   // K, V x double buffer
 };

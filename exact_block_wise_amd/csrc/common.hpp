@@ -44,6 +44,12 @@ __device__ __forceinline__ void mfma32_agpr(bf16x8 a, bf16x8 b, f32x16& c) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                : "+a"(c) : "v"(a), "v"(b));
 }
+// The same product with a zero accumulator operand (the first product of an
+// accumulator): nothing has to clear the AGPRs beforehand.
+__device__ __forceinline__ void mfma32_agpr_zero(bf16x8 a, bf16x8 b, f32x16& c) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+               : "=a"(c) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ void agpr_results_ready() {
   // covers the longest result latency of a 32x32 product (16 passes)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -140,6 +146,20 @@ __device__ __forceinline__ bf16x8 acc_half_to_bf16(const f32x16& s, int h) {
   return cvt8(s[8 * h + 0], s[8 * h + 1], s[8 * h + 2], s[8 * h + 3],
               s[8 * h + 4], s[8 * h + 5], s[8 * h + 6], s[8 * h + 7]);
 }
+
+// Row stride, in elements, of a bf16 LDS tile with DP columns that is read
+// both as rows (16-byte pieces, 16 lanes per pass) and as columns
+// (ds_read_b64_tr_b16: per half-wave four rows of 64 bytes).  With 64
+// four-byte banks, a stride of S banks puts the four rows of a column read at
+// banks 0, S, 2S, 3S (mod 64), each 16 banks wide, and the 16 rows of a row
+// read at 0, S, .., 15S, each 4 wide.  DP + 8 serves d = 64 and 80 (column
+// reads at most two-way conflicted, row reads free); at DP = 128 it gives
+// S = 4 (mod 64) and four-way conflicted column reads, and DP + 24 (S = 12)
+// keeps row reads free with column reads overlapping on 4 banks only.
+#ifndef EXATTN_STRIDE128
+#define EXATTN_STRIDE128 152
+#endif
+constexpr int tile_stride(int dp) { return dp == 128 ? EXATTN_STRIDE128 : dp + 8; }
 
 // Buffer resource over rows [0, rows) of a row-major tensor that starts at
 // `base`, rows `stride_bytes` apart and `row_bytes` long.  Raw buffer loads

@@ -53,7 +53,7 @@ constexpr float kLazy = 8.0f;  // log2 of the largest weight allowed before resc
 template <int D>
 struct FwdLds {
   static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int KS = DP + 8;                // row stride of the K and V tiles
+  static constexpr int KS = tile_stride(DP);       // row stride of the K and V tiles
   static constexpr int tile = fwdk::BN * KS;        // elements per tile
   static constexpr int bytes = 4 * tile * 2;        // K, V x double buffer
 };
