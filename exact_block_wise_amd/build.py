@@ -19,6 +19,14 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libexattn.so")
 SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "merge.hip", "short.hip"]
 
+# Per-source flags.  bwd.hip: the dK/dV kernels keep their gradient
+# accumulators in AGPRs through inline-assembly products, and a function that
+# names AGPRs in inline assembly otherwise gets the AGPR form for every
+# matrix product, so the score tiles S and dP would also land in AGPRs and
+# cost one v_accvgpr_read per element before the exponentials.  The VGPR form
+# leaves them in VGPRs (the dQ kernels of the file compile to the same code).
+SOURCE_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-munsafe-fp-atomics",
@@ -82,7 +90,7 @@ def build(verbose: bool = False, out_dir: str | None = None,
     jobs = []
     for src in SOURCES:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        jobs.append((obj, [cc, *HIPCC_FLAGS, *(extra_flags or []), "-c",
+        jobs.append((obj, [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *(extra_flags or []), "-c",
                            os.path.join(CSRC, src), "-o", obj]))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         for out in ex.map(lambda j: _run(j[1]), jobs):

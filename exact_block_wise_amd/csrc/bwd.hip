@@ -178,9 +178,30 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
     if constexpr (PARTS > 1) __builtin_amdgcn_sched_barrier(0);
   }
   prio_valu();
+  // d = 128, one key block per wave: the transposed dO / Q operands of both
+  // query halves are read here, ahead of the exponentials, so that the
+  // VALU work covers their latency (elsewhere they are read just before
+  // each product, and other waves cover it).  The LSE rows come first:
+  // LDS reads complete in order, and the exponentials wait only for them.
+  constexpr bool EARLY = PARTS > 1;
+  f32x4 l4s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l4s[i] = *reinterpret_cast<const f32x4*>(&lse2s[32 * nb + 8 * i + 4 * g]);
+  bf16x8 dob_e[EARLY ? 2 : 1][EARLY ? NDB : 1], qbv_e[EARLY ? 2 : 1][EARLY ? NDB : 1];
+  if constexpr (EARLY) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int t = 2 * nb + hh;
+        dob_e[hh][db] = tr_operand(dOs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+        qbv_e[hh][db] = tr_operand(Qs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * nb + 8 * i + 4 * g]);
+    const f32x4 l4 = l4s[i];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -208,8 +229,14 @@ __device__ __forceinline__ void dkdv_qblock(const bf16* Qs, const bf16* dOs, int
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16x8 dob = tr_operand(dOs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
-      const bf16x8 qbv = tr_operand(Qs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+      bf16x8 dob, qbv;
+      if constexpr (EARLY) {
+        dob = dob_e[hh][db];
+        qbv = qbv_e[hh][db];
+      } else {
+        dob = tr_operand(dOs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+        qbv = tr_operand(Qs + 32 * db, rs, 16 * t + 4 * g, 16 * t + 8 + 4 * g, lane);
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         // FIRST: the block's first products start the accumulators from zero
@@ -439,9 +466,12 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 // once per workgroup and stays there.  The workgroup then walks its share of
 // the head's 128-key blocks; each wave owns 32 keys of a block, holds their
 // K / V rows in registers, and loads the rows of its next block while it
-// computes the current one (so the key stream overlaps the matrix work).
+// computes the current one (so the key stream overlaps the matrix work):
+// into registers at d = 64 and 80, into its own LDS rows by direct-to-LDS
+// loads at d = 128, where the registers are needed for the accumulators.
 // No barrier is needed inside the key loop: the query side is read-only and
-// each wave's keys are its own.  dK and dV leave as each block completes.
+// each wave's keys and LDS rows are its own.  dK and dV leave as each block
+// completes.
 // --------------------------------------------------------------------------
 namespace resk {
 constexpr int QR = 128;  // resident query rows
@@ -454,7 +484,15 @@ struct ResLds {
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int RS = tile_stride(DP);                  // row stride of Q, dO
   static constexpr int stage = 32 * RS;                       // output rows per wave
-  static constexpr int bytes = 2 * resk::QR * RS * 2 + 2 * resk::QR * 4 + 4 * stage * 2;
+  // d = 128: the next key block's K and V rows reach LDS by direct-to-LDS
+  // loads instead of registers, which the accumulators need.  Each wave
+  // owns a region holding its 32 K and 32 V rows (row stride KS, whole 1 KB
+  // load instructions); its output staging reuses the region once the rows
+  // have been read into registers.
+  static constexpr bool kv_lds = D == 128;
+  static constexpr int KS = DP + 16;
+  static constexpr int region = kv_lds && 64 * KS > stage ? 64 * KS : stage;
+  static constexpr int bytes = 2 * resk::QR * RS * 2 + 2 * resk::QR * 4 + 4 * region * 2;
 };
 
 #ifndef EXATTN_DKDV_RESIDENT
@@ -476,7 +514,7 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31, g = lane >> 5;
-  bf16* const stage = reinterpret_cast<bf16*>(Ds + QR) + w * L::stage;  // this wave's output rows
+  bf16* const stage = reinterpret_cast<bf16*>(Ds + QR) + w * L::region;  // this wave's region
 
   int idx = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = idx % groups;
@@ -535,7 +573,34 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
   };
   bf16x8 kreg[1][KC], vreg[1][KC], knext[1][KC], vnext[1][KC];
   f32x16 dk[1][NDB], dv[1][NDB];
-  auto block = [&](int kb_) {
+  // K and V rows through LDS (L::kv_lds): piece p = 64 j + lane of load
+  // instruction j is row p / KCPR, 16-byte column p % KCPR of the wave's
+  // rows; lanes on a row's padding re-load its first piece
+  constexpr int KCPR = L::KS / 8, KNI = 32 * KCPR / 64;
+  static_assert(!L::kv_lds || (32 * KCPR) % 64 == 0, "whole instructions");
+  bf16* const kbuf = stage;
+  bf16* const vbuf = stage + 32 * L::KS;
+  auto load_kv_lds = [&](int kb_) {
+    const int kw = kb_ * KB + 32 * w;
+    const auto rk = rows_rsrc(kp + (int64_t)kw * a.ks.sn, a.Nkv - kw, 2 * a.ks.sn, 2 * D);
+    const auto rv = rows_rsrc(vp + (int64_t)kw * a.vs.sn, a.Nkv - kw, 2 * a.vs.sn, 2 * D);
+    const uint32_t kl = lds_address(kbuf), vl = lds_address(vbuf);
+#pragma unroll
+    for (int j = 0; j < KNI; ++j) {
+      const int pc = 64 * j + lane, r = pc / KCPR, ch = pc % KCPR;
+      const uint32_t col = 16 * (ch < D / 8 ? ch : 0);
+      buffer_load_lds16(rk, kl + 1024 * j, (uint32_t)(r * 2 * a.ks.sn) + col);
+      buffer_load_lds16(rv, vl + 1024 * j, (uint32_t)(r * 2 * a.vs.sn) + col);
+    }
+  };
+  auto read_kv_lds = [&] {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      kreg[0][kc] = load_bf16x8(&kbuf[ln * L::KS + 16 * kc + 8 * g]);
+      vreg[0][kc] = load_bf16x8(&vbuf[ln * L::KS + 16 * kc + 8 * g]);
+    }
+  };
+  auto block = [&](int kb_, bool next) {
     negate_rows(vreg);
     // the first query block's products start dK and dV from zero (no
     // clearing of the accumulators per key block)
@@ -549,6 +614,13 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
     // and the compiler treats a mix of both as unordered, so a wait for the
     // rows placed after the stores drains the stores as well, every block.
     wait_vmem();
+    if constexpr (L::kv_lds) {
+      if (next) {
+        // the next rows into registers before the staging reuses their LDS
+        read_kv_lds();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      }
+    }
     dkdv_store<D, 1>(a, b, h, seq_span(a, b, h), kb_ * KB + 32 * w, dk, dv, stage, lane);
   };
   load_kv(kb, kreg, vreg);
@@ -558,15 +630,23 @@ __global__ __launch_bounds__(resk::NT) void dkdv_resident_kernel(BwdArgs a, int 
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) asm volatile("" ::"v"(kreg[0][kc]), "v"(vreg[0][kc]));
   for (; kb + groups < nkb; kb += groups) {
-    load_kv(kb + groups, knext, vnext);
-    block(kb);
+    if constexpr (L::kv_lds) {
+      // the staging reads of the previous block are done before the rows
+      // land over them
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      load_kv_lds(kb + groups);
+      block(kb, true);
+    } else {
+      load_kv(kb + groups, knext, vnext);
+      block(kb, true);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      kreg[0][kc] = knext[0][kc];
-      vreg[0][kc] = vnext[0][kc];
+      for (int kc = 0; kc < KC; ++kc) {
+        kreg[0][kc] = knext[0][kc];
+        vreg[0][kc] = vnext[0][kc];
+      }
     }
   }
-  block(kb);
+  block(kb, false);
 }
 
 // --------------------------------------------------------------------------
