@@ -48,6 +48,8 @@ namespace fwdk {
 constexpr int BN = 64;
 constexpr int NT = 256;
 constexpr float kLazy = 8.0f;  // log2 of the largest weight allowed before rescaling
+// the largest partial sum of a lane's 32 weights that skips the row maxima
+constexpr float kSumBound = 8192.0f;  // 2^(kLazy + 5)
 }  // namespace fwdk
 
 template <int D>
@@ -158,74 +160,102 @@ void fwd_bf16_kernel(FwdArgs a) {
       const bool second = !TAIL || rem > 32;
       const int nchunks = TAIL ? (rem + 15) / 16 : 4;
       f32x16 s[2][NQB];
-      prio_mfma();
+      // (the memory fence keeps the compiler from reusing the first pass's
+      // scores in the second one, which would hold them in 32 more registers)
+      auto scores = [&] {
+        asm volatile("" ::: "memory");
+        prio_mfma();
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
-        if (cb == 1 && !second) break;
+          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = f32x16{};
+          if (cb == 1 && !second) break;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
+          for (int kc = 0; kc < KC; ++kc) {
+            const bf16x8 ka = load_bf16x8(&Kt[(32 * cb + ln) * KS + 16 * kc + 8 * g]);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
-        }
-      }
-      prio_valu();
-      if constexpr (TAIL) {
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const bool dead = j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3) >= n_kv;
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              if (dead) s[cb][qb][e] = -INFINITY;
+            for (int qb = 0; qb < NQB; ++qb) s[cb][qb] = mfma32(ka, qreg[qb][kc], s[cb][qb]);
           }
-      }
-      // row maxima; raise the reference (rescaling what O and l hold so
-      // far) only when a row's maximum exceeds it by more than 2^kLazy
-      float mx[NQB];
-      bool raise = false;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float m = s[0][qb][0];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) m = fmaxf(m, s[cb][qb][e]);
-        mx[qb] = max_halves(m);
-        raise |= mx[qb] > mref[qb] + lazy;
-      }
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const float mnew = fmaxf(mref[qb], mx[qb]);
-          const float alpha = fast_exp2((mref[qb] - mnew) * sl2);
-          mref[qb] = mnew;
-          lsum[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
         }
-      }
+        prio_valu();
+        if constexpr (TAIL) {
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const bool dead = j0 + 32 * cb + 8 * (e >> 2) + 4 * g + (e & 3) >= n_kv;
+#pragma unroll
+              for (int qb = 0; qb < NQB; ++qb)
+                if (dead) s[cb][qb][e] = -INFINITY;
+            }
+        }
+      };
       // P = exp2(sl2 (s - mref)) in place, and this lane's sum of its 32
       // weights per query block.  The sum is taken over the fp32 weights: a
       // peaky row's few dominant weights would carry their bf16 rounding
       // into the LSE.
+      float psum[NQB];
+      auto weigh = [&] {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float moff = mref[qb] * sl2;
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float moff = mref[qb] * sl2;
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+          for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float p = fast_exp2(fmaf(s[cb][qb][e], sl2, -moff));
-            s[cb][qb][e] = p;
-            part[e & 3] += p;
-          }
-        lsum[qb] += (part[0] + part[1]) + (part[2] + part[3]);
+            for (int e = 0; e < 16; ++e) {
+              const float p = fast_exp2(fmaf(s[cb][qb][e], sl2, -moff));
+              s[cb][qb][e] = p;
+              part[e & 3] += p;
+            }
+          psum[qb] = (part[0] + part[1]) + (part[2] + part[3]);
+        }
+      };
+      scores();
+      // After the first tile the weights are formed against the current
+      // reference first.  A partial sum of at most 2^(kLazy + 5) (a NaN or
+      // infinite one fails the test) bounds each of its 32 weights by that
+      // much, and then the tile needs no row maximum.  Otherwise, and on
+      // the first tile, the scores are formed again, the row maxima taken,
+      // and the reference raised (rescaling what O and l hold so far) where
+      // a row's maximum exceeds it by more than 2^kLazy.
+      bool slow = it == 0;
+      if (!slow) {
+        weigh();
+        bool big = false;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) big |= !(psum[qb] <= kSumBound);
+        slow = __builtin_amdgcn_ballot_w64(big) != 0;
+        if (slow) scores();
       }
+      if (slow) {
+        float mx[NQB];
+        bool raise = false;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float m = s[0][qb][0];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, s[cb][qb][e]);
+          mx[qb] = max_halves(m);
+          raise |= mx[qb] > mref[qb] + lazy;
+        }
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float mnew = fmaxf(mref[qb], mx[qb]);
+            const float alpha = fast_exp2((mref[qb] - mnew) * sl2);
+            mref[qb] = mnew;
+            lsum[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
+          }
+        }
+        weigh();
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) lsum[qb] += psum[qb];
       // O^T += V^T P^T over four 16-key chunks.  Chunk t = 2 cb + hh holds,
       // for slot group g, keys 16t + 4g + (0..3) and 16t + 8 + 4g + (0..3):
       // accumulator entries 8hh .. 8hh+7 of block cb.

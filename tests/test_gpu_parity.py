@@ -460,3 +460,36 @@ def test_resident_backward_both_halves(d, accumulate):
     got_dq = to_host(dq) - (to_host(base) if accumulate else 0.0)
     errs = check_grads([got_dq, to_host(dk), to_host(dv)], ref, "bf16", f"resident d={d}")
     _say(f"  resident d={d} acc={accumulate}: {['%.2e' % e for e in errs]}")
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_row_maximum_rising_in_later_tiles(d):
+    """Every query shares a direction u, and two late keys lie along it:
+    key 300 (scores up to about 6 above the first tile's maximum, around
+    the forward's lazy bound of 8 ln 2) and key 700 (at least 60 above it,
+    and for nearly every row more than 90, where weights taken against the
+    first tile's maximum would overflow fp32).  Each row's maximum therefore
+    rises in the middle of the key sequence, where the forward skips the row
+    maxima unless a partial sum shows a weight past its bound: both the skip
+    and the rescale run, and a missed rescale would give inf / NaN.
+
+    Forward only: with one key holding nearly all the weight, dQ nearly
+    vanishes and is ill-conditioned.  Taking D = dO . O from the bf16-rounded
+    O, as the backward does, moves it by about its own size: with key 700 at
+    48 u instead, that one rounding gives a relative dQ error of 1.008 in
+    fp64, so a relative tolerance on dQ cannot be met here."""
+    B, H, Nq, Nkv = 1, 2, 160, 1000
+    case = ("rising", d)
+    _say(f"case {case}")
+    x = synth.random_case(zlib.crc32(repr(case).encode()), B, H, Nq, Nkv, d, "bf16")
+    u = np.zeros(d, np.float32)
+    u[::3] = 1.0
+    u /= np.linalg.norm(u)
+    x["q"] = synth.round_to_bf16(x["q"] + 6.0 * u)
+    x["k"][:, :, 300] = synth.round_to_bf16(8.0 * u)
+    x["k"][:, :, 700] = synth.round_to_bf16(256.0 * u)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    s700 = scale * np.einsum("bhnd,bhd->bhn", x["q"], x["k"][:, :, 700])
+    s_first = scale * np.einsum("bhnd,bhmd->bhnm", x["q"], x["k"][:, :, :64]).max(-1)
+    assert np.all(s700 - s_first > 60) and np.mean(s700 - s_first > 90) > 0.95
+    run_case(x, "bf16", scale, check_bwd=False)
