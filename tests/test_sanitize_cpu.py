@@ -19,7 +19,10 @@ def test_abi_validation_under_asan_ubsan(tmp_path):
         lib = build.build(out_dir=str(tmp_path), sanitize=True)
     except RuntimeError as e:  # no hipcc / runtime in this environment
         pytest.skip(str(e))
-    env = {**os.environ, "EXATTN_LIB": lib, "LD_PRELOAD": runtime,
+    # the sanitizer runtime must come first; whatever the environment
+    # already preloads stays preloaded after it
+    pre = os.environ.get("LD_PRELOAD", "")
+    env = {**os.environ, "EXATTN_LIB": lib, "LD_PRELOAD": runtime + (":" + pre if pre else ""),
            "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=0:halt_on_error=1"}
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-s", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_abi_cpu.py")],
