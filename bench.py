@@ -612,7 +612,8 @@ def summary(line):
            "ms_per_step": line["ms_per_step"], "step_ms_stats": line["step_ms_stats"],
            "steps": line["steps"], "warmup": line["warmup"], "dtype": line["dtype"],
            "config": line["config"],
-           "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac")}}
+           "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac",
+                                          "traffic", "algorithmic_bytes") if k in r}}
     for k in ("cpu_baseline", "oracle_errors"):
         if k in line:
             out[k] = line[k]
