@@ -48,8 +48,14 @@ namespace fwdk {
 constexpr int BN = 64;
 constexpr int NT = 256;
 constexpr float kLazy = 8.0f;  // log2 of the largest weight allowed before rescaling
-// the largest partial sum of a lane's 32 weights that skips the row maxima
-constexpr float kSumBound = 8192.0f;  // 2^(kLazy + 5)
+// the largest partial sum of a lane's 32 weights that skips the row maxima:
+// 2^kLazy, so a tile is taken as it is only where the maxima would not have
+// raised the reference either.  (A looser bound, 2^(kLazy + 5), was faster
+// on the spatial shape but keeps stale references on peaky rows: their
+// dominant weight then carries bf16 rounding instead of being exactly 1
+// after a raise, and the O error of a peaky d = 128 case grew from 0.014 to
+// 0.022, past the 2e-2 tolerance once the output's own rounding adds in.)
+constexpr float kSumBound = 256.0f;
 }  // namespace fwdk
 
 template <int D>
@@ -213,7 +219,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       };
       scores();
       // After the first tile the weights are formed against the current
-      // reference first.  A partial sum of at most 2^(kLazy + 5) (a NaN or
+      // reference first.  A partial sum of at most 2^kLazy (a NaN or
       // infinite one fails the test) bounds each of its 32 weights by that
       // much, and then the tile needs no row maximum.  Otherwise, and on
       // the first tile, the scores are formed again, the row maxima taken,
